@@ -1,0 +1,111 @@
+"""Oracle for the MSDA forward core (test infrastructure only).
+
+A plain, slow, single-threaded CPU implementation of the multi-scale
+deformable attention core, written in C (``msda_oracle.c``) from the method's
+definition and loaded here with ctypes.  Only the tests, the smoke check and
+the benchmark's CPU-baseline leg may import this package; the HIP library
+never calls it and the two share no code.
+
+``build()`` compiles ``liboracle.so`` with gcc.  ``msda_oracle_forward`` and
+``msda3d_oracle_forward`` take the same tensors as the GPU entry points (on
+the CPU), widen value and attention weights exactly to float64, keep the
+sampling locations in float32 (the precision of the corner-index decision),
+and return the float64 result ``[N, Lq, M*D]``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "msda_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build() -> str:
+    """Compile the oracle into ``oracle/liboracle.so`` (always rebuilds)."""
+    tmp = _LIB_PATH + ".tmp"
+    cmd = ["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math",
+           "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    i64 = ctypes.c_int64
+    ptr = ctypes.c_void_p
+    for name in ("msda_oracle_forward", "msda3d_oracle_forward"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [ptr] * 6 + [i64] * 7
+    _lib = lib
+    return lib
+
+
+def _as_numpy(x, dtype):
+    """Exact conversion of a torch tensor or array to a contiguous numpy array."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().cpu()
+            if np.dtype(dtype) == np.float64:
+                x = x.to(torch.float64)  # exact for float32 and bfloat16
+            x = x.contiguous().numpy()
+    except ImportError:  # pragma: no cover - torch is always present here
+        pass
+    arr = np.ascontiguousarray(x)
+    if arr.dtype != np.dtype(dtype):
+        if np.dtype(dtype) == np.float32 and arr.dtype != np.float32:
+            raise TypeError("sampling_locations must be float32")
+        arr = np.ascontiguousarray(arr.astype(dtype))
+    return arr
+
+
+def _run(dims, value, spatial_shapes, level_start_index, sampling_locations,
+         attention_weights):
+    lib = _load()
+    v = _as_numpy(value, np.float64)
+    shapes = _as_numpy(spatial_shapes, np.int64)
+    lsi = _as_numpy(level_start_index, np.int64)
+    loc = _as_numpy(sampling_locations, np.float32)
+    aw = _as_numpy(attention_weights, np.float64)
+    if v.ndim != 4:
+        raise ValueError("value must be [N, S, M, D]")
+    N, S, M, D = v.shape
+    if loc.ndim != 6 or loc.shape[-1] != dims:
+        raise ValueError(f"sampling_locations must be [N, Lq, M, L, P, {dims}]")
+    _, Lq, _, L, P, _ = loc.shape
+    if aw.shape != loc.shape[:-1] or shapes.shape != (L, dims) or lsi.shape != (L,):
+        raise ValueError("inconsistent shapes")
+    out = np.empty((N, Lq, M * D), dtype=np.float64)
+    fn = lib.msda_oracle_forward if dims == 2 else lib.msda3d_oracle_forward
+    rc = fn(v.ctypes.data, shapes.ctypes.data, lsi.ctypes.data, loc.ctypes.data,
+            aw.ctypes.data, out.ctypes.data, N, S, M, D, Lq, L, P)
+    if rc != 0:
+        raise ValueError(f"oracle rejected its arguments (code {rc})")
+    return out
+
+
+def msda_oracle_forward(value, spatial_shapes, level_start_index,
+                        sampling_locations, attention_weights) -> np.ndarray:
+    """2D oracle: value [N,S,M,D], shapes [L,2]=(H,W), locations [N,Lq,M,L,P,2]."""
+    return _run(2, value, spatial_shapes, level_start_index, sampling_locations,
+                attention_weights)
+
+
+def msda3d_oracle_forward(value, spatial_shapes, level_start_index,
+                          sampling_locations, attention_weights) -> np.ndarray:
+    """3D oracle: value [N,S,M,D], shapes [L,3]=(Z,H,W), locations [...,3]."""
+    return _run(3, value, spatial_shapes, level_start_index, sampling_locations,
+                attention_weights)

@@ -1,0 +1,21 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line(
+        "markers", "gpu: needs an MI355X (runs the HIP library on cuda:0)")
+
+
+@pytest.fixture(scope="session", autouse=True)
+def _oracle_built():
+    """Compile the oracle once per session (gcc, seconds)."""
+    import oracle
+    oracle.build()
+    yield
