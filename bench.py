@@ -1,0 +1,240 @@
+#!/usr/bin/env python3
+"""Throughput of the MSDA forward core on one MI355X.
+
+One step = one msda_forward call over one batch of the Deformable-DETR
+encoder workload (N=2, 4 levels (100,167),(50,84),(25,42),(13,21), S=Lq=22223,
+M=8, D=32, L=4, P=4, fp32), inputs already resident in HBM.  Steps cycle over
+several distinct copies of the inputs whose total exceeds twice the 256 MB
+Infinity Cache, so each step reads its inputs from HBM rather than from a
+cache warmed by the previous step.
+
+Prints one JSON line: sampled points/s over the timed steps, achieved
+effective HBM GB/s of the kernel against the 8 TB/s peak (roofline), the
+oracle's CPU throughput on the same inputs (cpu_baseline), and the counter
+traffic recorded for this kernel under profiles/ when it is still current.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "sampled points/sec + achieved HBM GB/s (DETR encoder shape, 1 MI355X)"
+HBM_PEAK_GBPS = 8000.0
+MALL_BYTES = 256 << 20
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "msda_forward_counters.json")
+KERNEL_SOURCES = [
+    os.path.join(ROOT, "scale_deformable_attention_02_amd", "csrc", "msda_device.hpp"),
+    os.path.join(ROOT, "scale_deformable_attention_02_amd", "csrc", "msda_api.hip"),
+]
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def byte_counts(w):
+    """Algorithmic bytes of one launch.
+
+    U (compulsory): locations + weights + out + value, each moved once (value
+    capped at the gathered bytes when few queries touch it).
+    G (gathered): every corner row read once per sample, plus the streams.
+    """
+    samples = w.sampled_points
+    corners = 4 if w.dims == 2 else 8
+    loc = samples * w.dims * 4
+    attw = samples * 4
+    out = w.N * w.queries_per_image * w.M * w.D * w.out_itemsize
+    value = w.N * w.S * w.M * w.D * w.value_itemsize
+    gathered_value = samples * corners * w.D * w.value_itemsize
+    U = loc + attw + out + min(value, gathered_value)
+    G = loc + attw + out + gathered_value
+    return U, G
+
+
+def counters_for(workload_name: str):
+    """Per-launch HBM traffic from committed rocprofv3 counters, if current."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    with open(COUNTERS_FILE) as f:
+        data = json.load(f)
+    if data.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    entry = data.get("workloads", {}).get(workload_name)
+    if not entry:
+        return None
+    return entry.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(w, inp, max_points=60_000_000):
+    """Time the oracle (single-threaded C) on the same inputs, bounded."""
+    import numpy as np
+
+    from oracle import msda3d_oracle_forward, msda_oracle_forward
+
+    fn = msda_oracle_forward if w.dims == 2 else msda3d_oracle_forward
+    per_query = w.M * w.L * w.P
+    if w.sampled_points <= max_points:
+        nb, nq = w.N, w.queries_per_image
+        sample = "the whole workload"
+    else:
+        nb, nq = 1, max(1, max_points // per_query)
+        sample = f"queries 0..{nq - 1} of image 0"
+    value = inp["value"][:nb].double().numpy()
+    loc = np.ascontiguousarray(inp["sampling_locations"][:nb, :nq].numpy())
+    attw = inp["attention_weights"][:nb, :nq].double().numpy()
+    shapes = inp["spatial_shapes"].numpy()
+    starts = inp["level_start_index"].numpy()
+    t0 = time.perf_counter()
+    fn(value, shapes, starts, loc, attw)
+    dt = time.perf_counter() - t0
+    points = nb * nq * per_query
+    return {
+        "value": points / dt,
+        "unit": "sampled points/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{sample}: {points} sampled points in {dt:.2f} s, single-threaded C "
+                  f"oracle (fp64 accumulate) on {platform.processor() or platform.machine()}",
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="detr_encoder",
+                    help="workload name (default: the DETR encoder configuration)")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip timing the oracle (for profiler runs)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after timing, run one plain device copy of this many MiB "
+                         "(a known-size reference for HBM byte counters)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
+              "the core needs no communication, see the sharding notes in DESIGN.md",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    from scale_deformable_attention_02_amd import msda3d_forward, msda_forward
+    from scale_deformable_attention_02_amd.workloads import CONFIGS, make_inputs
+
+    w = CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    inp = make_inputs(w)
+    U, G = byte_counts(w)
+    copies = max(2, -(-(2 * MALL_BYTES + 1) // U))
+    base = {k: v.to(dev) for k, v in inp.items()}
+    sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(copies - 1)]
+    out_dt = torch.bfloat16 if w.out_dtype == "bf16" else torch.float32
+    outs = [torch.empty((w.N, w.queries_per_image, w.M * w.D), dtype=out_dt, device=dev)
+            for _ in range(copies)]
+    fwd = msda_forward if w.dims == 2 else msda3d_forward
+
+    def step(i):
+        d = sets[i % copies]
+        fwd(d["value"], d["spatial_shapes"], d["level_start_index"],
+            d["sampling_locations"], d["attention_weights"], out=outs[i % copies])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    kernel_s = statistics.mean(launch_ms) / 1e3
+
+    # back-to-back on one input set: inputs stay in L2/Infinity Cache
+    warm_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(20)]
+    for a, b in warm_ev:
+        a.record(stream)
+        step(0)
+        b.record(stream)
+    torch.cuda.synchronize()
+    warm_s = statistics.median([a.elapsed_time(b) for a, b in warm_ev]) / 1e3
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    points = w.sampled_points
+    ms_per_step = wall / args.steps * 1e3
+    achieved = U / kernel_s / 1e9
+    traffic = counters_for(w.name)
+    result = {
+        "metric": METRIC,
+        "value": points / (wall / args.steps),
+        "unit": "sampled points/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.value_dtype == "bf16" else "f32",
+        "data": "synthetic (seeded; no dataset or trained weights)",
+        "config": {
+            "workload": w.name, "N": w.N, "levels": [list(s) for s in w.shapes], "S": w.S,
+            "Lq": w.queries_per_image, "M": w.M, "D": w.D, "L": w.L, "P": w.P,
+            "value_dtype": w.value_dtype, "out_dtype": w.out_dtype,
+            "input_copies_cycled": copies,
+            "parallelism": "single GPU",
+        },
+        "achieved_hbm_gbps": achieved,
+        "gathered_gbps": G / kernel_s / 1e9,
+        "kernel_us_mean": kernel_s * 1e6,
+        "kernel_us_median": statistics.median(launch_ms) * 1e3,
+        "kernel_us_warm_median": warm_s * 1e6,
+        "bytes_per_launch": {"compulsory": U, "gathered": G},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": traffic,
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, inp)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,126 @@
+/*
+ * msda.h - C ABI of the MI355X multi-scale deformable attention (MSDA) core.
+ *
+ * The operation (both entry points): for every batch n, query q, head m and
+ * channel d
+ *
+ *   out[n][q][m*D + d] = sum_{l<L} sum_{p<P} A[n][q][m][l][p] *
+ *                        interp(value[n][level l][.][m][d], loc[n][q][m][l][p])
+ *
+ * This is the per-head inner sum of the deformable attention equation on the
+ * "Deformable Attention Module" page (codewithpapers; the W'_m and W_m
+ * projections are not part of it, heads are concatenated), extended to a
+ * pyramid of L levels with P points each and one weighted sum over the L*P
+ * samples ("3D Attention That Knows Where to Look", section on the
+ * "Multi-Scale" in MSDA).  interp is bilinear over the 4 pixels around the
+ * point ("What is Deformable Attention", item (3)) for msda_forward and
+ * trilinear over the 8 corners of the voxel cube for msda3d_forward ("3D
+ * Attention...", 2D->3D change list: (x, y) -> (x, y, z), (H, W) -> (D, H, W),
+ * locations (..., P, 2) -> (..., P, 3)).
+ *
+ * Conventions the pages leave open, fixed here:
+ *   - normalized location x in [0, 1] spans the outer pixel edges; pixel j's
+ *     centre is at (j + 0.5) / W, i.e. pixel-space x_hat = fmaf(x, W, -0.5f)
+ *     rounded once in fp32 (the same as grid_sample, align_corners=False);
+ *   - a corner outside its level contributes zero (zero padding); weights of
+ *     the other corners are not renormalised; a sample whose coordinate is
+ *     NaN/Inf or outside (-1, extent) contributes zero;
+ *   - location component 0 = x runs along W (fastest), 1 = y along H, 2 = z
+ *     along the depth; level pixels are flattened row-major, s = start + i*W + j
+ *     (3D: start + (k*H + i)*W + j);
+ *   - attention weights are used as given (the caller applies the softmax).
+ *
+ * Memory: every tensor pointer is a DEVICE pointer to contiguous row-major
+ * data owned by the caller.  The library allocates, frees and synchronises
+ * nothing and keeps no state: calls are re-entrant and thread-safe.  Work is
+ * enqueued on `stream` (a hipStream_t; NULL = the null stream) and the call
+ * returns without waiting.  `out` is overwritten, never accumulated into, and
+ * must not alias an input.
+ *
+ * Errors: the return value is an msda_status.  Every argument check below is
+ * done on the host before any HIP call, so a rejected call touches neither the
+ * device nor the stream.  spatial_shapes and level_start_index live on the
+ * device and are NOT read by the host: that every level is >= 1 pixel, that
+ * level_start_index holds the prefix sums of the level sizes and that their
+ * total is S is the caller's contract (a violation reads wrong pixels of
+ * `value` but never outside `value`, which every gather is bounds-checked
+ * against).
+ */
+#ifndef MSDA_H
+#define MSDA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of `value` and, independently, of `out`.  Accumulation is
+ * always fp32; a bf16 `out` is the fp32 result rounded to nearest-even. */
+typedef enum {
+    MSDA_F32 = 0,   /* IEEE binary32 */
+    MSDA_BF16 = 1   /* bfloat16      */
+} msda_dtype;
+
+typedef enum {
+    MSDA_OK = 0,
+    MSDA_ERR_NULL = 1,        /* a required pointer is NULL                */
+    MSDA_ERR_DIM = 2,         /* a size is negative, or S, M, D, L, P < 1  */
+    MSDA_ERR_DTYPE = 3,       /* value_dtype or out_dtype is not an
+                                 msda_dtype                                */
+    MSDA_ERR_UNSUPPORTED = 4, /* D not a multiple of 16 bytes of value, or
+                                 D*sizeof(value) > 1024 bytes, L > 16, or
+                                 L*P > 64                                  */
+    MSDA_ERR_ALIGN = 5,       /* value/out not 16-byte aligned, locations,
+                                 weights not 4-byte aligned, shapes/starts
+                                 not 8-byte aligned                        */
+    MSDA_ERR_OVERFLOW = 6,    /* one image's value (S*M*D elements) is
+                                 2^31 bytes or more                        */
+    MSDA_ERR_LAUNCH = 7       /* the HIP launch failed                     */
+} msda_status;
+
+/*
+ * 2D multi-scale deformable attention forward (bilinear).
+ *
+ *   value               [N][S][M][D], value_dtype; S = sum_l H_l*W_l
+ *   spatial_shapes      int64 [L][2] = (H_l, W_l)
+ *   level_start_index   int64 [L], start of level l in S (prefix sums)
+ *   sampling_locations  float [N][Lq][M][L][P][2] = normalized (x, y)
+ *   attention_weights   float [N][Lq][M][L][P]
+ *   out                 [N][Lq][M*D], out_dtype, fully overwritten
+ *   out_dtype           MSDA_F32 (the fp32 accumulator) or MSDA_BF16
+ *   stream              hipStream_t (void* so this header needs no HIP)
+ *
+ * N == 0 or Lq == 0 is a successful no-op (pointers may then be NULL).
+ */
+int msda_forward(const void* value, int value_dtype,
+                 const int64_t* spatial_shapes,
+                 const int64_t* level_start_index,
+                 const float* sampling_locations,
+                 const float* attention_weights, void* out, int out_dtype,
+                 int64_t N, int64_t S, int64_t M, int64_t D,
+                 int64_t Lq, int64_t L, int64_t P, void* stream);
+
+/*
+ * 3D multi-scale deformable attention forward (trilinear over 8 corners).
+ * Same as msda_forward except:
+ *   spatial_shapes      int64 [L][3] = (Z_l, H_l, W_l) (depth, height, width)
+ *   sampling_locations  float [N][Lq][M][L][P][3] = normalized (x, y, z)
+ *   S = sum_l Z_l*H_l*W_l
+ */
+int msda3d_forward(const void* value, int value_dtype,
+                   const int64_t* spatial_shapes,
+                   const int64_t* level_start_index,
+                   const float* sampling_locations,
+                   const float* attention_weights, void* out, int out_dtype,
+                   int64_t N, int64_t S, int64_t M, int64_t D,
+                   int64_t Lq, int64_t L, int64_t P, void* stream);
+
+/* Static, human-readable description of a status code (never NULL). */
+const char* msda_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSDA_H */

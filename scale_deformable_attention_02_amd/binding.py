@@ -1,0 +1,161 @@
+"""Python binding of the C ABI in ``include/msda.h`` (argument marshalling only).
+
+``msda_forward`` and ``msda3d_forward`` take torch tensors that already live
+on the GPU, check dtypes/shapes/contiguity, allocate ``out`` with torch when
+the caller passes none, and call the same-named C entry point of
+``libmsda.so`` on torch's current HIP stream.  Every step of the computation
+runs in the library's kernels.  If ``libmsda.so`` has not been built, the
+first call raises; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmsda.so")
+
+MSDA_F32 = 0
+MSDA_BF16 = 1
+
+STATUS = {
+    0: "MSDA_OK",
+    1: "MSDA_ERR_NULL",
+    2: "MSDA_ERR_DIM",
+    3: "MSDA_ERR_DTYPE",
+    4: "MSDA_ERR_UNSUPPORTED",
+    5: "MSDA_ERR_ALIGN",
+    6: "MSDA_ERR_OVERFLOW",
+    7: "MSDA_ERR_LAUNCH",
+}
+
+# Every symbol include/msda.h declares.
+EXPORTED = ("msda_forward", "msda3d_forward", "msda_status_string")
+
+_lib = None
+
+
+class MsdaError(RuntimeError):
+    """A non-zero msda_status from the library."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library() -> ctypes.CDLL:
+    """Load ``libmsda.so`` (once); raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is missing: build it with "
+            "scale_deformable_attention_02_amd._build.build()")
+    lib = ctypes.CDLL(_LIB_PATH)
+    i64 = ctypes.c_int64
+    vp = ctypes.c_void_p
+    for name in ("msda_forward", "msda3d_forward"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [vp, ctypes.c_int, vp, vp, vp, vp, vp, ctypes.c_int,
+                       i64, i64, i64, i64, i64, i64, i64, vp]
+    lib.msda_status_string.restype = ctypes.c_char_p
+    lib.msda_status_string.argtypes = [ctypes.c_int]
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().msda_status_string(int(status)).decode()
+
+
+def raw_call(dims: int, value_ptr: int, value_dtype: int, shapes_ptr: int,
+             starts_ptr: int, loc_ptr: int, attw_ptr: int, out_ptr: int,
+             out_dtype: int, N: int, S: int, M: int, D: int, Lq: int, L: int, P: int,
+             stream: int = 0) -> int:
+    """Call the C entry point with raw pointers; returns the msda_status."""
+    lib = load_library()
+    fn = lib.msda_forward if dims == 2 else lib.msda3d_forward
+    return fn(value_ptr, value_dtype, shapes_ptr, starts_ptr, loc_ptr, attw_ptr,
+              out_ptr, out_dtype, N, S, M, D, Lq, L, P, stream)
+
+
+def _dtype_code(dtype: torch.dtype, what: str) -> int:
+    if dtype == torch.float32:
+        return MSDA_F32
+    if dtype == torch.bfloat16:
+        return MSDA_BF16
+    raise TypeError(f"{what} must be float32 or bfloat16, got {dtype}")
+
+
+def _forward(dims: int, value: torch.Tensor, spatial_shapes: torch.Tensor,
+             level_start_index: torch.Tensor, sampling_locations: torch.Tensor,
+             attention_weights: torch.Tensor, out: Optional[torch.Tensor],
+             out_dtype: Optional[torch.dtype],
+             stream: Optional[torch.cuda.Stream]) -> torch.Tensor:
+    tensors = dict(value=value, spatial_shapes=spatial_shapes,
+                   level_start_index=level_start_index,
+                   sampling_locations=sampling_locations,
+                   attention_weights=attention_weights)
+    for name, t in tensors.items():
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    code = _dtype_code(value.dtype, "value")
+    if spatial_shapes.dtype != torch.int64 or level_start_index.dtype != torch.int64:
+        raise TypeError("spatial_shapes and level_start_index must be int64")
+    if sampling_locations.dtype != torch.float32 or attention_weights.dtype != torch.float32:
+        raise TypeError("sampling_locations and attention_weights must be float32")
+    if value.dim() != 4:
+        raise ValueError("value must be [N, S, M, D]")
+    N, S, M, D = value.shape
+    if sampling_locations.dim() != 6 or sampling_locations.shape[-1] != dims:
+        raise ValueError(f"sampling_locations must be [N, Lq, M, L, P, {dims}]")
+    n2, Lq, m2, L, P, _ = sampling_locations.shape
+    if (n2, m2) != (N, M) or attention_weights.shape != sampling_locations.shape[:-1]:
+        raise ValueError("sampling_locations / attention_weights do not match value")
+    if spatial_shapes.shape != (L, dims) or level_start_index.shape != (L,):
+        raise ValueError("spatial_shapes / level_start_index do not match L")
+    if out is None:
+        dt = value.dtype if out_dtype is None else out_dtype
+        out = torch.empty((N, Lq, M * D), dtype=dt, device=value.device)
+    elif (out.shape != (N, Lq, M * D) or not out.is_contiguous()
+          or out.device != value.device or (out_dtype is not None and out.dtype != out_dtype)):
+        raise ValueError("out must be a contiguous [N, Lq, M*D] tensor on value's device")
+    out_code = _dtype_code(out.dtype, "out")
+    s = stream if stream is not None else torch.cuda.current_stream(value.device)
+    status = raw_call(dims, value.data_ptr(), code, spatial_shapes.data_ptr(),
+                      level_start_index.data_ptr(), sampling_locations.data_ptr(),
+                      attention_weights.data_ptr(), out.data_ptr(), out_code,
+                      N, S, M, D, Lq, L, P, s.cuda_stream)
+    if status != 0:
+        raise MsdaError(status, status_string(status))
+    return out
+
+
+def msda_forward(value, spatial_shapes, level_start_index, sampling_locations,
+                 attention_weights, out=None, out_dtype=None, stream=None) -> torch.Tensor:
+    """2D MSDA forward: value [N,S,M,D] (fp32/bf16), spatial_shapes [L,2]=(H,W),
+    level_start_index [L], sampling_locations [N,Lq,M,L,P,2], attention_weights
+    [N,Lq,M,L,P]; returns [N, Lq, M*D].  The output dtype is ``out``'s, else
+    ``out_dtype``, else value's (fp32 accumulation either way; bf16 output is
+    rounded to nearest-even).  Asynchronous on ``stream`` (default: torch's
+    current stream)."""
+    return _forward(2, value, spatial_shapes, level_start_index, sampling_locations,
+                    attention_weights, out, out_dtype, stream)
+
+
+def msda3d_forward(value, spatial_shapes, level_start_index, sampling_locations,
+                   attention_weights, out=None, out_dtype=None, stream=None) -> torch.Tensor:
+    """3D MSDA forward (trilinear): spatial_shapes [L,3]=(Z,H,W), locations
+    [N,Lq,M,L,P,3] = (x, y, z); otherwise as ``msda_forward``."""
+    return _forward(3, value, spatial_shapes, level_start_index, sampling_locations,
+                    attention_weights, out, out_dtype, stream)

@@ -1,0 +1,211 @@
+// C ABI of the MSDA forward core (declared in include/msda.h): argument
+// validation, launch-shape selection and the kernel dispatch.
+//
+// Nothing here allocates, frees or synchronises; every argument check runs on
+// the host before the first HIP call.
+#include "msda.h"
+
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "msda_device.hpp"
+
+namespace {
+
+using msda::FastDiv;
+using msda::Params;
+
+FastDiv make_fast_div(uint32_t d) {
+    uint32_t l = 0;
+    while ((uint64_t{1} << l) < d) ++l;
+    const uint64_t shift = 31 + l;
+    const uint64_t mul = ((uint64_t{1} << shift) + d - 1) / d;  // <= 2^32 - 1
+    return FastDiv{static_cast<uint32_t>(mul), static_cast<uint32_t>(shift)};
+}
+
+int floor_log2(int64_t x) {
+    int r = 0;
+    while ((int64_t{2} << r) <= x) ++r;
+    return r;
+}
+
+int ceil_log2(int64_t x) {
+    int r = 0;
+    while ((int64_t{1} << r) < x) ++r;
+    return r;
+}
+
+template <typename TV, typename TO, int DIM, int CPL>
+void launch_one(const Params& p, hipStream_t stream) {
+    hipLaunchKernelGGL((msda::msda_forward_kernel<TV, TO, DIM, CPL>), dim3(p.num_blocks),
+                       dim3(msda::kBlockThreads), 0, stream, p);
+}
+
+template <typename TV, typename TO, int DIM>
+void launch_cpl(int cpl, const Params& p, hipStream_t stream) {
+    switch (cpl) {
+        case 1: launch_one<TV, TO, DIM, 1>(p, stream); break;
+        case 2: launch_one<TV, TO, DIM, 2>(p, stream); break;
+        case 4: launch_one<TV, TO, DIM, 4>(p, stream); break;
+        case 8: launch_one<TV, TO, DIM, 8>(p, stream); break;
+        case 16: launch_one<TV, TO, DIM, 16>(p, stream); break;
+        case 32: launch_one<TV, TO, DIM, 32>(p, stream); break;
+        default: launch_one<TV, TO, DIM, 64>(p, stream); break;
+    }
+}
+
+template <int DIM>
+void launch(int value_dtype, int out_dtype, int cpl, const Params& p, hipStream_t stream) {
+    if (value_dtype == MSDA_F32) {
+        if (out_dtype == MSDA_F32)
+            launch_cpl<float, float, DIM>(cpl, p, stream);
+        else
+            launch_cpl<float, msda::Bf16, DIM>(cpl, p, stream);
+    } else {
+        if (out_dtype == MSDA_F32)
+            launch_cpl<msda::Bf16, float, DIM>(cpl, p, stream);
+        else
+            launch_cpl<msda::Bf16, msda::Bf16, DIM>(cpl, p, stream);
+    }
+}
+
+bool known_dtype(int dt) { return dt == MSDA_F32 || dt == MSDA_BF16; }
+
+bool aligned(const void* ptr, uintptr_t a) {
+    return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) == 0;
+}
+
+template <int DIM>
+int forward(const void* value, int value_dtype, const int64_t* spatial_shapes,
+            const int64_t* level_start_index, const float* sampling_locations,
+            const float* attention_weights, void* out, int out_dtype, int64_t N,
+            int64_t S, int64_t M, int64_t D, int64_t Lq, int64_t L, int64_t P,
+            void* stream) {
+    if (N < 0 || Lq < 0 || S < 1 || M < 1 || D < 1 || L < 1 || P < 1)
+        return MSDA_ERR_DIM;
+    if (!known_dtype(value_dtype) || !known_dtype(out_dtype)) return MSDA_ERR_DTYPE;
+    if (N == 0 || Lq == 0) return MSDA_OK;
+    if (!value || !spatial_shapes || !level_start_index || !sampling_locations ||
+        !attention_weights || !out)
+        return MSDA_ERR_NULL;
+
+    const int64_t elem = value_dtype == MSDA_F32 ? 4 : 2;
+    const int64_t out_elem = out_dtype == MSDA_F32 ? 4 : 2;
+    const int64_t head_bytes = D * elem;
+    const int64_t out_head_bytes = D * out_elem;
+    if (head_bytes % 16 != 0 || head_bytes > 16 * msda::kWave) return MSDA_ERR_UNSUPPORTED;
+    if (L > msda::kMaxLevels || L * P > msda::kMaxSamplesPerTile) return MSDA_ERR_UNSUPPORTED;
+
+    if (!aligned(value, 16) || !aligned(out, 16) || !aligned(sampling_locations, 4) ||
+        !aligned(attention_weights, 4) || !aligned(spatial_shapes, 8) ||
+        !aligned(level_start_index, 8))
+        return MSDA_ERR_ALIGN;
+
+    // 32-bit byte offsets inside one launch's value slice, and 32-bit tile ids
+    const int64_t kLimit = int64_t{1} << 31;
+    if (S >= kLimit || M >= kLimit) return MSDA_ERR_OVERFLOW;
+    const int64_t image_bytes = S * M * head_bytes;
+    if (image_bytes >= kLimit) return MSDA_ERR_OVERFLOW;
+    const int64_t tiles_per_image = Lq * M;
+    if (Lq >= kLimit || tiles_per_image >= kLimit / 2) return MSDA_ERR_OVERFLOW;
+
+    // Launch shape.  CPL lanes cover one head row in 16-byte chunks; the
+    // NG = 64 / CPL point groups of a wave are split over T tiles, G groups
+    // per tile, each group taking NI of the tile's L*P samples.
+    const int64_t LP = L * P;
+    const int64_t nchunk = head_bytes / 16;
+    const int cpl = 1 << ceil_log2(nchunk);
+    const int ng = msda::kWave / cpl;
+    const int tiles_fit = 1 << floor_log2(msda::kWave / LP);
+    const int T = tiles_fit < ng ? tiles_fit : ng;
+    const int G = ng / T;
+    const int NI = static_cast<int>((LP + G - 1) / G);
+
+    // Images per launch: keep the value slice below 2^31 bytes (the
+    // out-of-range marker) and the tile count below 2^31.
+    int64_t nb = (kLimit - 1) / image_bytes;
+    const int64_t nb_tiles = (kLimit / 2) / tiles_per_image;
+    if (nb_tiles < nb) nb = nb_tiles;
+    if (nb > N) nb = N;
+
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    const int64_t tiles_per_block = int64_t{msda::kWavesPerBlock} * T;
+    for (int64_t n0 = 0; n0 < N; n0 += nb) {
+        const int64_t nbatch = (N - n0 < nb) ? N - n0 : nb;
+        const int64_t tiles = nbatch * tiles_per_image;
+        Params p{};
+        p.value = static_cast<const char*>(value) + n0 * image_bytes;
+        p.shapes = spatial_shapes;
+        p.starts = level_start_index;
+        p.loc = sampling_locations + n0 * tiles_per_image * LP * DIM;
+        p.attw = attention_weights + n0 * tiles_per_image * LP;
+        p.out = static_cast<char*>(out) + n0 * tiles_per_image * out_head_bytes;
+        p.tiles = static_cast<uint32_t>(tiles);
+        p.value_bytes = static_cast<uint32_t>(nbatch * image_bytes);
+        p.row_bytes = static_cast<uint32_t>(M * head_bytes);
+        p.head_bytes = static_cast<uint32_t>(head_bytes);
+        p.out_head_bytes = static_cast<uint32_t>(out_head_bytes);
+        p.image_bytes = static_cast<uint32_t>(image_bytes);
+        p.num_blocks = static_cast<uint32_t>((tiles + tiles_per_block - 1) / tiles_per_block);
+        p.M = static_cast<int32_t>(M);
+        p.L = static_cast<int32_t>(L);
+        p.P = static_cast<int32_t>(P);
+        p.LP = static_cast<int32_t>(LP);
+        p.T = T;
+        p.log2G = ceil_log2(G);
+        p.NI = NI;
+        p.nchunk = static_cast<int32_t>(nchunk);
+        p.div_M = make_fast_div(static_cast<uint32_t>(M));
+        p.div_LqM = make_fast_div(static_cast<uint32_t>(tiles_per_image));
+        p.div_P = make_fast_div(static_cast<uint32_t>(P));
+
+        launch<DIM>(value_dtype, out_dtype, cpl, p, hs);
+        if (hipGetLastError() != hipSuccess) return MSDA_ERR_LAUNCH;
+    }
+    return MSDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int msda_forward(const void* value, int value_dtype, const int64_t* spatial_shapes,
+                 const int64_t* level_start_index, const float* sampling_locations,
+                 const float* attention_weights, void* out, int out_dtype, int64_t N,
+                 int64_t S, int64_t M, int64_t D, int64_t Lq, int64_t L, int64_t P,
+                 void* stream) {
+    return forward<2>(value, value_dtype, spatial_shapes, level_start_index,
+                      sampling_locations, attention_weights, out, out_dtype, N, S, M, D, Lq,
+                      L, P, stream);
+}
+
+int msda3d_forward(const void* value, int value_dtype, const int64_t* spatial_shapes,
+                   const int64_t* level_start_index, const float* sampling_locations,
+                   const float* attention_weights, void* out, int out_dtype, int64_t N,
+                   int64_t S, int64_t M, int64_t D, int64_t Lq, int64_t L, int64_t P,
+                   void* stream) {
+    return forward<3>(value, value_dtype, spatial_shapes, level_start_index,
+                      sampling_locations, attention_weights, out, out_dtype, N, S, M, D, Lq,
+                      L, P, stream);
+}
+
+const char* msda_status_string(int status) {
+    switch (status) {
+        case MSDA_OK: return "ok";
+        case MSDA_ERR_NULL: return "a required pointer is NULL";
+        case MSDA_ERR_DIM: return "bad dimension (negative, or S, M, D, L, P < 1)";
+        case MSDA_ERR_DTYPE: return "unknown value or out dtype";
+        case MSDA_ERR_UNSUPPORTED:
+            return "unsupported shape (D*sizeof(value) must be a multiple of 16 and <= 1024 "
+                   "bytes, L <= 16, L*P <= 64)";
+        case MSDA_ERR_ALIGN:
+            return "misaligned pointer (value/out need 16 bytes, locations/weights 4, "
+                   "shapes/starts 8)";
+        case MSDA_ERR_OVERFLOW: return "one image's value tensor is 2^31 bytes or larger";
+        case MSDA_ERR_LAUNCH: return "HIP kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

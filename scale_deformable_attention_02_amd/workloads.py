@@ -49,6 +49,7 @@ class Workload:
     box: Tuple[float, float] = (-0.1, 1.1)  # range of "uniform" locations
     seed: int = 1000
     description: str = field(default="", compare=False)
+    out_dtype: str = "f32"          # "f32" or "bf16" (accumulation is fp32)
 
     @property
     def L(self) -> int:
@@ -76,6 +77,10 @@ class Workload:
     def value_itemsize(self) -> int:
         return 2 if self.value_dtype == "bf16" else 4
 
+    @property
+    def out_itemsize(self) -> int:
+        return 2 if self.out_dtype == "bf16" else 4
+
     def with_(self, **kw) -> "Workload":
         return replace(self, **kw)
 
@@ -99,8 +104,8 @@ CONFIGS: Dict[str, Workload] = {
     "detr_encoder_bf16_b8": Workload(
         "detr_encoder_bf16_b8", 2, 8, LEVELS_2D, None, 8, 32, 4, "bf16",
         "pixel_centres", 0.02, (0.0, 1.0), 1004,
-        "Deformable-DETR encoder at scale, bf16 value/out, fp32 "
-        "locations/weights: N=8, S=Lq=22223"),
+        "Deformable-DETR encoder at scale, bf16 value, fp32 "
+        "locations/weights/accumulation/out: N=8, S=Lq=22223"),
     "volume3d": Workload(
         "volume3d", 3, 1, LEVELS_3D, None, 8, 32, 4, "f32", "pixel_centres",
         0.02, (0.0, 1.0), 1005,
