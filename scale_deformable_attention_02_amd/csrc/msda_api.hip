@@ -102,13 +102,11 @@ int forward(const void* value, int value_dtype, const int64_t* spatial_shapes,
         !aligned(level_start_index, 8))
         return MSDA_ERR_ALIGN;
 
-    // 32-bit byte offsets inside one launch's value slice, and 32-bit tile ids
+    // One image's value must be addressable with 32-bit byte offsets.
     const int64_t kLimit = int64_t{1} << 31;
-    if (S >= kLimit || M >= kLimit) return MSDA_ERR_OVERFLOW;
+    if (S >= kLimit || M >= kLimit || Lq >= kLimit) return MSDA_ERR_OVERFLOW;
     const int64_t image_bytes = S * M * head_bytes;
     if (image_bytes >= kLimit) return MSDA_ERR_OVERFLOW;
-    const int64_t tiles_per_image = Lq * M;
-    if (Lq >= kLimit || tiles_per_image >= kLimit / 2) return MSDA_ERR_OVERFLOW;
 
     // Launch shape.  CPL lanes cover one head row in 16-byte chunks; the
     // NG = 64 / CPL point groups of a wave are split over T tiles, G groups
@@ -122,46 +120,70 @@ int forward(const void* value, int value_dtype, const int64_t* spatial_shapes,
     const int G = ng / T;
     const int NI = static_cast<int>((LP + G - 1) / G);
 
-    // Images per launch: keep the value slice below 2^31 bytes (the
-    // out-of-range marker) and the tile count below 2^31.
-    int64_t nb = (kLimit - 1) / image_bytes;
-    const int64_t nb_tiles = (kLimit / 2) / tiles_per_image;
-    if (nb_tiles < nb) nb = nb_tiles;
-    if (nb > N) nb = N;
+    // Work per launch: whole images while the value slice, the locations and
+    // the tile count stay below 2^31 bytes / 2^30 tiles (32-bit buffer
+    // offsets); otherwise one image at a time, split into query ranges.
+    const int64_t loc_per_query = M * LP * DIM * 4;
+    const int64_t attw_per_query = M * LP * 4;
+    const int64_t kTileLimit = int64_t{1} << 30;
+    int64_t nb = 0, nq = Lq;
+    if (Lq * loc_per_query < kLimit && Lq * M < kTileLimit) {
+        nb = (kLimit - 1) / image_bytes;
+        const int64_t by_loc = (kLimit - 1) / (Lq * loc_per_query);
+        const int64_t by_tiles = (kTileLimit - 1) / (Lq * M);
+        if (by_loc < nb) nb = by_loc;
+        if (by_tiles < nb) nb = by_tiles;
+        if (nb > N) nb = N;
+    } else {
+        nb = 1;
+        nq = (kLimit - 1) / loc_per_query;
+        const int64_t by_tiles = (kTileLimit - 1) / M;
+        if (by_tiles < nq) nq = by_tiles;
+    }
 
     const hipStream_t hs = static_cast<hipStream_t>(stream);
-    const int64_t tiles_per_block = int64_t{msda::kWavesPerBlock} * T;
     for (int64_t n0 = 0; n0 < N; n0 += nb) {
         const int64_t nbatch = (N - n0 < nb) ? N - n0 : nb;
-        const int64_t tiles = nbatch * tiles_per_image;
-        Params p{};
-        p.value = static_cast<const char*>(value) + n0 * image_bytes;
-        p.shapes = spatial_shapes;
-        p.starts = level_start_index;
-        p.loc = sampling_locations + n0 * tiles_per_image * LP * DIM;
-        p.attw = attention_weights + n0 * tiles_per_image * LP;
-        p.out = static_cast<char*>(out) + n0 * tiles_per_image * out_head_bytes;
-        p.tiles = static_cast<uint32_t>(tiles);
-        p.value_bytes = static_cast<uint32_t>(nbatch * image_bytes);
-        p.row_bytes = static_cast<uint32_t>(M * head_bytes);
-        p.head_bytes = static_cast<uint32_t>(head_bytes);
-        p.out_head_bytes = static_cast<uint32_t>(out_head_bytes);
-        p.image_bytes = static_cast<uint32_t>(image_bytes);
-        p.num_blocks = static_cast<uint32_t>((tiles + tiles_per_block - 1) / tiles_per_block);
-        p.M = static_cast<int32_t>(M);
-        p.L = static_cast<int32_t>(L);
-        p.P = static_cast<int32_t>(P);
-        p.LP = static_cast<int32_t>(LP);
-        p.T = T;
-        p.log2G = ceil_log2(G);
-        p.NI = NI;
-        p.nchunk = static_cast<int32_t>(nchunk);
-        p.div_M = make_fast_div(static_cast<uint32_t>(M));
-        p.div_LqM = make_fast_div(static_cast<uint32_t>(tiles_per_image));
-        p.div_P = make_fast_div(static_cast<uint32_t>(P));
+        for (int64_t q0 = 0; q0 < Lq; q0 += nq) {
+            const int64_t nquery = (Lq - q0 < nq) ? Lq - q0 : nq;
+            const int64_t waves_per_slice = (nquery + T - 1) / T;
+            const int64_t waves = nbatch * M * waves_per_slice;
+            const int64_t first_row = (n0 * Lq + q0) * M;
+            Params p{};
+            p.value = static_cast<const char*>(value) + n0 * image_bytes;
+            p.shapes = spatial_shapes;
+            p.starts = level_start_index;
+            p.loc = sampling_locations + first_row * LP * DIM;
+            p.attw = attention_weights + first_row * LP;
+            p.out = static_cast<char*>(out) + first_row * out_head_bytes;
+            p.value_bytes = static_cast<uint32_t>(nbatch * image_bytes);
+            p.loc_bytes = static_cast<uint32_t>(nbatch * nquery * loc_per_query);
+            p.attw_bytes = static_cast<uint32_t>(nbatch * nquery * attw_per_query);
+            p.row_bytes = static_cast<uint32_t>(M * head_bytes);
+            p.head_bytes = static_cast<uint32_t>(head_bytes);
+            p.out_head_bytes = static_cast<uint32_t>(out_head_bytes);
+            p.image_bytes = static_cast<uint32_t>(image_bytes);
+            p.num_blocks = static_cast<uint32_t>((waves + msda::kWavesPerBlock - 1) /
+                                                 msda::kWavesPerBlock);
+            p.waves = static_cast<uint32_t>(waves);
+            p.M = static_cast<int32_t>(M);
+            p.Lq = static_cast<int32_t>(Lq);
+            p.nq = static_cast<int32_t>(nquery);
+            p.L = static_cast<int32_t>(L);
+            p.P = static_cast<int32_t>(P);
+            p.LP = static_cast<int32_t>(LP);
+            p.T = T;
+            p.log2G = ceil_log2(G);
+            p.NI = NI;
+            p.nchunk = static_cast<int32_t>(nchunk);
+            p.wps = static_cast<uint32_t>(waves_per_slice);
+            p.div_wps = make_fast_div(static_cast<uint32_t>(waves_per_slice));
+            p.div_P = make_fast_div(static_cast<uint32_t>(P));
+            p.div_M = make_fast_div(static_cast<uint32_t>(M));
 
-        launch<DIM>(value_dtype, out_dtype, cpl, p, hs);
-        if (hipGetLastError() != hipSuccess) return MSDA_ERR_LAUNCH;
+            launch<DIM>(value_dtype, out_dtype, cpl, p, hs);
+            if (hipGetLastError() != hipSuccess) return MSDA_ERR_LAUNCH;
+        }
     }
     return MSDA_OK;
 }
@@ -202,7 +224,8 @@ const char* msda_status_string(int status) {
         case MSDA_ERR_ALIGN:
             return "misaligned pointer (value/out need 16 bytes, locations/weights 4, "
                    "shapes/starts 8)";
-        case MSDA_ERR_OVERFLOW: return "one image's value tensor is 2^31 bytes or larger";
+        case MSDA_ERR_OVERFLOW:
+            return "one image's value tensor is 2^31 bytes or larger (or S, M, Lq >= 2^31)";
         case MSDA_ERR_LAUNCH: return "HIP kernel launch failed";
         default: return "unknown status";
     }

@@ -7,13 +7,22 @@
 // Attention That Knows Where to Look": multi-scale L x P sum and the 2D->3D
 // change list).
 //
+// Tile order.  A launch covers nb images x a range of nq queries, cut into
+// slices (n, m) of nq queries each, head-major.  Every wave takes T
+// consecutive queries of one slice (the last wave of a slice may run past nq:
+// those tiles are dead), so (n, m) is uniform per wave and lives in scalar
+// registers.  Consecutive workgroups - after the XCD renumbering below, the
+// whole stream of one XCD - walk one head's queries: the value rows they
+// gather are that head's D-channel slices, a footprint 1/M of the pyramid that
+// fits the XCD's L2.
+//
 // Work decomposition (per wave of 64 lanes):
-//   * The wave owns T consecutive tiles.  Their T*L*P samples are contiguous in
-//     sampling_locations / attention_weights, so they are read once, coalesced.
+//   * The wave owns T consecutive tiles (same head, consecutive queries).
 //   * Phase A (one lane per sample): pixel-space transform, range test, corner
-//     indices and corner weights pre-multiplied by A, written to this wave's
-//     LDS slot array.  The ~30 VALU operations of this step run once per sample
-//     instead of once per channel lane.
+//     offsets and corner weights pre-multiplied by A, written to this wave's
+//     LDS slot array.  These ~40 VALU operations run once per sample instead
+//     of once per channel lane.  Branch-free: invalid samples and corners get
+//     weight 0 and an out-of-range offset.
 //   * Phase B (lanes = CPL channel chunks x NG point groups): a chunk is 16 bytes
 //     of one value row (4 fp32 or 8 bf16 channels); the G groups that share a
 //     tile split its samples between them.  Each lane reads its group's slot
@@ -24,7 +33,8 @@
 //
 // Out-of-range corners are given a buffer offset past the end of the value
 // buffer: a buffer load there returns 0 without touching memory, so the zero
-// padding costs neither a branch nor memory traffic.
+// padding costs neither a branch nor memory traffic.  Every global read is a
+// buffer load bounded by its tensor's byte size.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -37,8 +47,8 @@ constexpr int kWavesPerBlock = 4;
 constexpr int kBlockThreads = kWave * kWavesPerBlock;
 constexpr int kMaxLevels = 16;
 constexpr int kMaxSamplesPerTile = 64;  // L * P
-// Offset given to a corner outside its level: >= 2^31 >= the byte size of any
-// value buffer a launch is given, so the buffer load returns zero.
+// Offset given to anything that must read as zero: >= 2^31 > the byte size of
+// every buffer a launch is given, so the buffer load returns 0.
 constexpr uint32_t kOutOfRange = 0x80000000u;
 // Descriptor word 3 of a raw (stride 0, untyped) buffer on gfx9-family parts.
 constexpr int kBufferWord3 = 0x00020000;
@@ -60,23 +70,26 @@ struct Params {
     const void* value;            // this launch's images, [nb][S][M][D]
     const int64_t* shapes;        // [L][DIM]
     const int64_t* starts;        // [L]
-    const float* loc;             // [nb][Lq][M][L][P][DIM]
-    const float* attw;            // [nb][Lq][M][L][P]
-    void* out;                    // [nb][Lq][M*D]
-    uint32_t tiles;               // nb * Lq * M
+    const float* loc;             // at (n0, q0): rows ((n*Lq + q)*M + m), LP*DIM floats each
+    const float* attw;            // at (n0, q0): rows of LP floats
+    void* out;                    // at (n0, q0): rows of D outputs
     uint32_t value_bytes;         // byte size of this launch's value slice
+    uint32_t loc_bytes;           // byte size of the locations this launch may read
+    uint32_t attw_bytes;          // byte size of the weights this launch may read
     uint32_t row_bytes;           // M * D * sizeof(value): one pixel, all heads
     uint32_t head_bytes;          // D * sizeof(value): one pixel, one head
     uint32_t out_head_bytes;      // D * sizeof(out): one (n, q, m) output run
     uint32_t image_bytes;         // S * M * D * sizeof(value)
     uint32_t num_blocks;          // grid size
-    int32_t M, L, P, LP;
-    int32_t T;                    // tiles per wave
+    uint32_t waves;               // nb * M * waves_per_slice
+    int32_t M, Lq, nq, L, P, LP;  // Lq: queries per image; nq: queries per launch
+    int32_t T;                    // tiles (consecutive queries) per wave
     int32_t log2G;                // log2(point groups per tile)
     int32_t NI;                   // sample iterations per group in phase B
     int32_t nchunk;               // 16-byte chunks per head row (<= CPL)
-    FastDiv div_M;                // tile -> (n*Lq + q)
-    FastDiv div_LqM;              // tile -> n
+    uint32_t wps;                 // waves per slice, ceil(nq / T)
+    FastDiv div_wps;              // wave -> slice n*M + m
+    FastDiv div_M;                // slice -> n
     FastDiv div_P;                // sample -> level
 };
 
@@ -91,14 +104,19 @@ struct __align__(16) Slot {
 
 // Workgroups are dispatched round-robin over the 8 XCDs (block b runs on XCD
 // b % 8).  Renumber them so that each XCD walks one contiguous range of
-// tiles: neighbouring queries, which sample overlapping pixels, then share
-// that XCD's L2 instead of being spread over all eight.
+// tiles: with the head-major tile order that range is one or two heads'
+// queries, whose value rows stay in that XCD's L2.
 __device__ __forceinline__ uint32_t xcd_contiguous_block(uint32_t b, uint32_t nb) {
     constexpr uint32_t kXcds = 8;
     const uint32_t per = nb / kXcds, extra = nb % kXcds;
     const uint32_t xcd = b % kXcds, k = b / kXcds;
     return xcd < extra ? xcd * (per + 1) + k
                        : extra * (per + 1) + (xcd - extra) * per + k;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
+                                             static_cast<int>(bytes), kBufferWord3);
 }
 
 template <typename T>
@@ -173,74 +191,60 @@ struct OutTraits<Bf16> {
     }
 };
 
-// Phase A for one sample: fill the slot from its location, weight and level.
-// Level metadata: lm = (W, H, Z, start).
+// Phase A for one sample, branch-free.  xyz: normalized location; a: its
+// attention weight (0 for a dead lane); lm = (W, H, Z, start) of its level;
+// head_base: byte offset of (image n, pixel 0, head m) in the value slice.
 template <int DIM>
-__device__ __forceinline__ void make_slot(const float* loc, float a, int4 lm,
-                                          uint32_t head_base, uint32_t row_bytes,
-                                          Slot<DIM == 2 ? 4 : 8>& sl) {
+__device__ __forceinline__ Slot<DIM == 2 ? 4 : 8> make_slot(const float (&xyz)[DIM], float a,
+                                                            bool live, int4 lm,
+                                                            uint32_t head_base,
+                                                            uint32_t row_bytes) {
+    constexpr int NC = DIM == 2 ? 4 : 8;
     const int W = lm.x, H = lm.y, Z = lm.z;
     const float Wf = static_cast<float>(W), Hf = static_cast<float>(H);
+    const float Zf = static_cast<float>(Z);
     // pixel-space coordinates: pixel j's centre is at normalized (j + 0.5) / W
-    const float xh = fmaf(loc[0], Wf, -0.5f);
-    const float yh = fmaf(loc[1], Hf, -0.5f);
-    float zh = 0.0f;
-    bool inside = xh > -1.0f && xh < Wf && yh > -1.0f && yh < Hf;
-    if (DIM == 3) {
-        const float Zf = static_cast<float>(Z);
-        zh = fmaf(loc[2], Zf, -0.5f);
-        inside = inside && zh > -1.0f && zh < Zf;
-    }
-    if (!inside) return;  // NaN, +-Inf and far-away samples land here
+    const float xh = fmaf(xyz[0], Wf, -0.5f);
+    const float yh = fmaf(xyz[1], Hf, -0.5f);
+    const float zh = DIM == 3 ? fmaf(xyz[2], Zf, -0.5f) : 0.0f;
+    // NaN fails every comparison, +-Inf and far samples fail one
+    bool inside = live && xh > -1.0f && xh < Wf && yh > -1.0f && yh < Hf;
+    if (DIM == 3) inside = inside && zh > -1.0f && zh < Zf;
 
-    const float x0f = floorf(xh), y0f = floorf(yh);
-    const float fx = xh - x0f, fy = yh - y0f;  // exact
+    // keep floor/int conversion defined for samples that are dropped anyway
+    const float xs = inside ? xh : 0.0f, ys = inside ? yh : 0.0f, zs = inside ? zh : 0.0f;
+    const float x0f = floorf(xs), y0f = floorf(ys), z0f = floorf(zs);
+    const float fx = xs - x0f, fy = ys - y0f, fz = zs - z0f;  // exact
     const int x0 = static_cast<int>(x0f), y0 = static_cast<int>(y0f);
-    const bool vx0 = x0 >= 0, vx1 = x0 + 1 < W;
-    const bool vy0 = y0 >= 0, vy1 = y0 + 1 < H;
-    const float wx0 = 1.0f - fx, wx1 = fx;
-    const float wy0 = 1.0f - fy, wy1 = fy;
+    const int z0 = static_cast<int>(z0f);
+    const float aw = inside ? a : 0.0f;
 
-    // byte offset of corner (z0, y0, x0); may wrap below zero for a corner at
-    // index -1, which is then masked out
-    int pix = lm.w + y0 * W + x0;
-    float wz0 = 1.0f, wz1 = 0.0f;
-    bool vz0 = true, vz1 = false;
-    int z0 = 0;
-    if (DIM == 3) {
-        const float z0f = floorf(zh);
-        const float fz = zh - z0f;
-        z0 = static_cast<int>(z0f);
-        vz0 = z0 >= 0;
-        vz1 = z0 + 1 < Z;
-        wz0 = 1.0f - fz;
-        wz1 = fz;
-        pix += z0 * H * W;
-    }
-    const uint32_t o000 = head_base + static_cast<uint32_t>(pix) * row_bytes;
+    const bool vx[2] = {x0 >= 0, x0 + 1 < W};
+    const bool vy[2] = {y0 >= 0, y0 + 1 < H};
+    const bool vz[2] = {z0 >= 0, z0 + 1 < Z};
+    const float wx[2] = {1.0f - fx, fx};
+    const float wy[2] = {1.0f - fy, fy};
+    const float wz[2] = {1.0f - fz, fz};
+
+    // byte offset of corner (z0, y0, x0); wraps for a corner at index -1, which
+    // is masked out (all offsets are exact modulo 2^32)
+    const int zy = DIM == 3 ? z0 * H + y0 : y0;
+    const int pix = zy * W + x0 + lm.w;
+    const uint32_t o000 = static_cast<uint32_t>(pix) * row_bytes + head_base;
     const uint32_t dx = row_bytes;
     const uint32_t dy = static_cast<uint32_t>(W) * row_bytes;
+    const uint32_t dz = static_cast<uint32_t>(H * W) * row_bytes;
 
+    Slot<NC> sl;
 #pragma unroll
-    for (int cz = 0; cz < (DIM == 3 ? 2 : 1); ++cz) {
-        const bool vz = cz ? vz1 : vz0;
-        const float wz = cz ? wz1 : wz0;
-        const uint32_t oz = o000 + (cz ? static_cast<uint32_t>(H * W) * row_bytes : 0u);
-#pragma unroll
-        for (int cy = 0; cy < 2; ++cy) {
-            const bool vy = cy ? vy1 : vy0;
-            const float wy = cy ? wy1 : wy0;
-#pragma unroll
-            for (int cx = 0; cx < 2; ++cx) {
-                const bool vx = cx ? vx1 : vx0;
-                const float wx = cx ? wx1 : wx0;
-                const int k = cz * 4 + cy * 2 + cx;
-                const bool ok = vz && vy && vx;
-                sl.off[k] = ok ? oz + (cy ? dy : 0u) + (cx ? dx : 0u) : kOutOfRange;
-                sl.w[k] = ok ? (a * wz) * (wy * wx) : 0.0f;
-            }
-        }
+    for (int k = 0; k < NC; ++k) {
+        const int cx = k & 1, cy = (k >> 1) & 1, cz = k >> 2;
+        const bool ok = inside && vx[cx] && vy[cy] && (DIM == 2 || vz[cz]);
+        const float wzk = DIM == 3 ? wz[cz] : 1.0f;
+        sl.off[k] = ok ? o000 + (cz ? dz : 0u) + (cy ? dy : 0u) + (cx ? dx : 0u) : kOutOfRange;
+        sl.w[k] = ok ? (aw * wzk) * (wy[cy] * wx[cx]) : 0.0f;
     }
+    return sl;
 }
 
 template <typename TV, typename TO, int DIM, int CPL>
@@ -249,31 +253,41 @@ __global__ __launch_bounds__(kBlockThreads) void msda_forward_kernel(Params p) {
     constexpr int NG = kWave / CPL;          // point groups per wave
     constexpr int VEC = ValueTraits<TV>::kVec;
 
-    __shared__ int4 meta[kMaxLevels];
+    __shared__ int4 smeta[kMaxSamplesPerTile];   // (W, H, Z, start) of sample s's level
     __shared__ Slot<NC> slots[kWavesPerBlock][kWave];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
 
-    if (tid < p.L) {
+    if (tid < p.LP) {
+        const int l = static_cast<int>(fast_div(static_cast<uint32_t>(tid), p.div_P));
         int4 lm;
         if (DIM == 2) {
-            lm.x = static_cast<int>(p.shapes[2 * tid + 1]);
-            lm.y = static_cast<int>(p.shapes[2 * tid + 0]);
+            lm.x = static_cast<int>(p.shapes[2 * l + 1]);
+            lm.y = static_cast<int>(p.shapes[2 * l + 0]);
             lm.z = 1;
         } else {
-            lm.x = static_cast<int>(p.shapes[3 * tid + 2]);
-            lm.y = static_cast<int>(p.shapes[3 * tid + 1]);
-            lm.z = static_cast<int>(p.shapes[3 * tid + 0]);
+            lm.x = static_cast<int>(p.shapes[3 * l + 2]);
+            lm.y = static_cast<int>(p.shapes[3 * l + 1]);
+            lm.z = static_cast<int>(p.shapes[3 * l + 0]);
         }
-        lm.w = static_cast<int>(p.starts[tid]);
-        meta[tid] = lm;
+        lm.w = static_cast<int>(p.starts[l]);
+        smeta[tid] = lm;
     }
-    __syncthreads();
 
+    // wave -> slice (n, m) and first query q0, all wave-uniform
     const uint32_t blk = xcd_contiguous_block(blockIdx.x, p.num_blocks);
-    const uint32_t tile0 = (blk * kWavesPerBlock + wave) * static_cast<uint32_t>(p.T);
+    const uint32_t wave_id =
+        __builtin_amdgcn_readfirstlane(blk * kWavesPerBlock + static_cast<uint32_t>(wave));
+    const bool wave_live = wave_id < p.waves;
+    const uint32_t slice = fast_div(wave_id, p.div_wps);
+    const uint32_t q0 = (wave_id - slice * p.wps) * static_cast<uint32_t>(p.T);
+    const uint32_t n = fast_div(slice, p.div_M);
+    const uint32_t m = slice - n * static_cast<uint32_t>(p.M);
+    // location/weight/output row of tile t is row0 + t*M
+    const uint32_t row0 = (n * static_cast<uint32_t>(p.Lq) + q0) * static_cast<uint32_t>(p.M) + m;
+    const uint32_t head_base = n * p.image_bytes + m * p.head_bytes;
     const int G = 1 << p.log2G;
 
     // ---- Phase A: lane k fills slot k = i*NG + g (iteration i of group g).
@@ -281,24 +295,34 @@ __global__ __launch_bounds__(kBlockThreads) void msda_forward_kernel(Params p) {
         const int i = lane / NG, g = lane % NG;
         const int t = g >> p.log2G, j = g & (G - 1);
         const int s = i * G + j;
-        const uint32_t tile = tile0 + static_cast<uint32_t>(t);
-        Slot<NC> sl;
-#pragma unroll
-        for (int k = 0; k < NC; ++k) {
-            sl.off[k] = kOutOfRange;
-            sl.w[k] = 0.0f;
+        const bool live = wave_live && i < p.NI && s < p.LP &&
+                          q0 + static_cast<uint32_t>(t) < static_cast<uint32_t>(p.nq);
+        const int s_c = live ? s : 0;
+        // sample index relative to row0 * LP
+        const uint32_t rel = static_cast<uint32_t>(t) * static_cast<uint32_t>(p.M * p.LP) +
+                             static_cast<uint32_t>(s_c);
+        const uint32_t sidx0 = row0 * static_cast<uint32_t>(p.LP);
+
+        const __amdgpu_buffer_rsrc_t rloc = buffer_of(p.loc, p.loc_bytes);
+        const __amdgpu_buffer_rsrc_t rattw = buffer_of(p.attw, p.attw_bytes);
+        const uint32_t loc_off = live ? (sidx0 + rel) * (DIM * 4u) : kOutOfRange;
+        const uint32_t attw_off = live ? (sidx0 + rel) * 4u : kOutOfRange;
+        float xyz[DIM];
+        if constexpr (DIM == 2) {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b64(rloc, loc_off, 0, 0);
+            xyz[0] = __uint_as_float(v[0]);
+            xyz[1] = __uint_as_float(v[1]);
+        } else {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b96(rloc, loc_off, 0, 0);
+            xyz[0] = __uint_as_float(v[0]);
+            xyz[1] = __uint_as_float(v[1]);
+            xyz[2] = __uint_as_float(v[2]);
         }
-        if (i < p.NI && s < p.LP && tile < p.tiles) {
-            const size_t sidx = static_cast<size_t>(tile) * p.LP + s;
-            const uint32_t nq = fast_div(tile, p.div_M);
-            const uint32_t m = tile - nq * static_cast<uint32_t>(p.M);
-            const uint32_t n = fast_div(tile, p.div_LqM);
-            const uint32_t head_base = n * p.image_bytes + m * p.head_bytes;
-            const int l = static_cast<int>(fast_div(static_cast<uint32_t>(s), p.div_P));
-            make_slot<DIM>(p.loc + sidx * DIM, p.attw[sidx], meta[l], head_base,
-                           p.row_bytes, sl);
-        }
-        slots[wave][lane] = sl;
+        const float a = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rattw, attw_off, 0, 0));
+
+        __syncthreads();  // smeta is ready
+        slots[wave][lane] =
+            make_slot<DIM>(xyz, a, live, smeta[s_c], head_base, p.row_bytes);
     }
     __syncthreads();
 
@@ -308,15 +332,14 @@ __global__ __launch_bounds__(kBlockThreads) void msda_forward_kernel(Params p) {
     // lanes past the head's last chunk (D*size not a power-of-two multiple of
     // 16 bytes) re-read the last chunk and never store
     const uint32_t lane_off = static_cast<uint32_t>(min(c, p.nchunk - 1)) * 16u;
-    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<void*>(p.value), 0, static_cast<int>(p.value_bytes), kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rsrc = buffer_of(p.value, p.value_bytes);
 
     float acc[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) acc[e] = 0.0f;
 
     const Slot<NC>* my = &slots[wave][g];
-#pragma unroll 2
+#pragma unroll 4
     for (int i = 0; i < p.NI; ++i) {
         const Slot<NC> sl = my[i * NG];
         uint32_t raw[NC][4];
@@ -343,9 +366,10 @@ __global__ __launch_bounds__(kBlockThreads) void msda_forward_kernel(Params p) {
         for (int e = 0; e < VEC; ++e) acc[e] += __shfl_xor(acc[e], s, kWave);
     }
 
-    const uint32_t tile = tile0 + static_cast<uint32_t>(t);
-    if (j == 0 && c < p.nchunk && tile < p.tiles) {
-        char* dst = static_cast<char*>(p.out) + static_cast<size_t>(tile) * p.out_head_bytes +
+    if (j == 0 && c < p.nchunk && wave_live &&
+        q0 + static_cast<uint32_t>(t) < static_cast<uint32_t>(p.nq)) {
+        const uint32_t row = row0 + static_cast<uint32_t>(t * p.M);
+        char* dst = static_cast<char*>(p.out) + static_cast<size_t>(row) * p.out_head_bytes +
                     static_cast<size_t>(c) * (VEC * sizeof(TO));
         OutTraits<TO>::template store<VEC>(dst, acc);
     }

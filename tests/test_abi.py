@@ -113,7 +113,7 @@ def test_overflow(lib):
     assert call(S=(1 << 31) // (8 * 32 * 4), M=8, D=32) == OVERFLOW
     assert call(S=1 << 31, M=1, D=4) == OVERFLOW
     assert call(Lq=1 << 31) == OVERFLOW
-    assert call(Lq=1 << 27, M=8) == OVERFLOW     # 2^30 tiles in one image
+    assert call(M=1 << 31, D=4) == OVERFLOW
 
 
 def test_binding_rejects_cpu_tensors(lib):
