@@ -9,12 +9,27 @@
 
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "msda_device.hpp"
+
+// Staged-kernel tuning (bytes of LDS for staged levels per workgroup, target
+// number of workgroups per launch, smallest launch worth staging).
+#ifndef MSDA_STAGE_BUDGET
+#define MSDA_STAGE_BUDGET (34 * 1024 + 512)
+#endif
+#ifndef MSDA_STAGED_TARGET_WGS
+#define MSDA_STAGED_TARGET_WGS 2048
+#endif
+#ifndef MSDA_STAGED_MIN_TILES
+#define MSDA_STAGED_MIN_TILES 65536
+#endif
 
 namespace {
 
 using msda::FastDiv;
 using msda::Params;
+using msda::StagedParams;
 
 FastDiv make_fast_div(uint32_t d) {
     uint32_t l = 0;
@@ -42,21 +57,45 @@ void launch_one(const Params& p, hipStream_t stream) {
                        dim3(msda::kBlockThreads), 0, stream, p);
 }
 
-template <typename TV, typename TO, int DIM>
-void launch_cpl(int cpl, const Params& p, hipStream_t stream) {
+template <typename TV, typename TO, int DIM, int CPL>
+void launch_staged_one(const StagedParams& sp, hipStream_t stream) {
+    static_assert(MSDA_STAGE_BUDGET <= 64 * 1024, "dynamic LDS above the default limit");
+    if constexpr (DIM == 2)  // the staged kernel is only launched for 2D pyramids
+        hipLaunchKernelGGL((msda::msda_forward_staged_kernel<TV, TO, DIM, CPL>),
+                           dim3(sp.p.num_blocks), dim3(msda::kStagedThreads), sp.stage_bytes,
+                           stream, sp);
+}
+
+// Kernel selection by CPL (lanes per head row), then by value/out type.
+template <typename TV, typename TO, int DIM, typename P>
+void launch_cpl(int cpl, const P& p, hipStream_t stream) {
+    constexpr bool staged = std::is_same<P, StagedParams>::value;
     switch (cpl) {
-        case 1: launch_one<TV, TO, DIM, 1>(p, stream); break;
-        case 2: launch_one<TV, TO, DIM, 2>(p, stream); break;
-        case 4: launch_one<TV, TO, DIM, 4>(p, stream); break;
-        case 8: launch_one<TV, TO, DIM, 8>(p, stream); break;
-        case 16: launch_one<TV, TO, DIM, 16>(p, stream); break;
-        case 32: launch_one<TV, TO, DIM, 32>(p, stream); break;
-        default: launch_one<TV, TO, DIM, 64>(p, stream); break;
+#define MSDA_CASE(C)                                          \
+    case C:                                                   \
+        if constexpr (staged)                                 \
+            launch_staged_one<TV, TO, DIM, C>(p, stream);     \
+        else                                                  \
+            launch_one<TV, TO, DIM, C>(p, stream);            \
+        break;
+        MSDA_CASE(1)
+        MSDA_CASE(2)
+        MSDA_CASE(4)
+        MSDA_CASE(8)
+        MSDA_CASE(16)
+        MSDA_CASE(32)
+        default:
+            if constexpr (staged)
+                launch_staged_one<TV, TO, DIM, 64>(p, stream);
+            else
+                launch_one<TV, TO, DIM, 64>(p, stream);
+            break;
+#undef MSDA_CASE
     }
 }
 
-template <int DIM>
-void launch(int value_dtype, int out_dtype, int cpl, const Params& p, hipStream_t stream) {
+template <int DIM, typename P>
+void launch(int value_dtype, int out_dtype, int cpl, const P& p, hipStream_t stream) {
     if (value_dtype == MSDA_F32) {
         if (out_dtype == MSDA_F32)
             launch_cpl<float, float, DIM>(cpl, p, stream);
@@ -178,8 +217,37 @@ int forward(const void* value, int value_dtype, const int64_t* spatial_shapes,
             p.nchunk = static_cast<int32_t>(nchunk);
             p.wps = static_cast<uint32_t>(waves_per_slice);
             p.div_wps = make_fast_div(static_cast<uint32_t>(waves_per_slice));
-            p.div_P = make_fast_div(static_cast<uint32_t>(P));
             p.div_M = make_fast_div(static_cast<uint32_t>(M));
+            p.div_P = make_fast_div(static_cast<uint32_t>(P));
+
+            // Staged kernel: large 2D launches whose phase-B iterations are
+            // level-pure (G divides P), with ~MSDA_STAGED_TARGET_WGS
+            // workgroups splitting each slice's chunks of kStagedWaves * T
+            // queries between them.  (3D pyramids' coarsest level is rarely
+            // small enough to copy whole: 8^3 voxels of 32 fp32 channels are
+            // 64 KB; there the direct kernel is faster.)
+            const int64_t tiles = nbatch * M * nquery;
+            if (DIM == 2 && P % G == 0 && tiles >= MSDA_STAGED_MIN_TILES) {
+                const int64_t pass = int64_t{msda::kStagedWaves} * T;
+                const int64_t slices = nbatch * M;
+                const int64_t chunks = (nquery + pass - 1) / pass;   // per slice
+                int64_t wgs_per_slice = (MSDA_STAGED_TARGET_WGS + slices - 1) / slices;
+                if (wgs_per_slice > chunks) wgs_per_slice = chunks;
+                if (wgs_per_slice < 1) wgs_per_slice = 1;
+                int64_t stage = (S + 1) * head_bytes;
+                if (stage > MSDA_STAGE_BUDGET) stage = MSDA_STAGE_BUDGET;
+                stage = stage / 16 * 16;
+                StagedParams sp{};
+                sp.p = p;
+                sp.p.num_blocks = static_cast<uint32_t>(slices * wgs_per_slice);
+                sp.wgs_per_slice = static_cast<uint32_t>(wgs_per_slice);
+                sp.div_wgs = make_fast_div(static_cast<uint32_t>(wgs_per_slice));
+                sp.stage_bytes = static_cast<uint32_t>(stage);
+                sp.ipl = static_cast<int32_t>(P / G);
+                launch<DIM>(value_dtype, out_dtype, cpl, sp, hs);
+                if (hipGetLastError() != hipSuccess) return MSDA_ERR_LAUNCH;
+                continue;
+            }
 
             launch<DIM>(value_dtype, out_dtype, cpl, p, hs);
             if (hipGetLastError() != hipSuccess) return MSDA_ERR_LAUNCH;

@@ -52,6 +52,21 @@ constexpr int kMaxSamplesPerTile = 64;  // L * P
 constexpr uint32_t kOutOfRange = 0x80000000u;
 // Descriptor word 3 of a raw (stride 0, untyped) buffer on gfx9-family parts.
 constexpr int kBufferWord3 = 0x00020000;
+// Cache policy of the streaming reads (locations, weights): read once, so
+// marked non-temporal (the buffer instruction's nt bit) to leave L2 to the
+// value rows that are gathered many times.
+#ifndef MSDA_STREAM_AUX
+#define MSDA_STREAM_AUX 2
+#endif
+// Output rows are written once and never read back here: non-temporal stores.
+#ifndef MSDA_NT_STORE
+#define MSDA_NT_STORE 1
+#endif
+// Phase-B iterations issued together (4 corners each).
+#ifndef MSDA_GATHER_UNROLL
+#define MSDA_GATHER_UNROLL 4
+#endif
+constexpr int kGatherUnroll = MSDA_GATHER_UNROLL;
 
 // floor(x / d) for 0 <= x < 2^31 as (x * mul) >> shift.  With l = ceil(log2 d),
 // shift = 31 + l and mul = ceil(2^shift / d) = (2^shift + e) / d, 0 <= e < d:
@@ -160,14 +175,28 @@ struct ValueTraits<Bf16> {
 template <typename TO>
 struct OutTraits;
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <typename V>
+__device__ __forceinline__ void store_out(V* dst, V v) {
+    if (MSDA_NT_STORE)
+        __builtin_nontemporal_store(v, dst);
+    else
+        *dst = v;
+}
+
 template <>
 struct OutTraits<float> {
     template <int VEC>
     __device__ __forceinline__ static void store(void* dst, const float (&acc)[VEC]) {
-        float4* d = reinterpret_cast<float4*>(dst);
+        f32x4* d = reinterpret_cast<f32x4*>(dst);
 #pragma unroll
-        for (int h = 0; h < VEC / 4; ++h)
-            d[h] = make_float4(acc[4 * h], acc[4 * h + 1], acc[4 * h + 2], acc[4 * h + 3]);
+        for (int h = 0; h < VEC / 4; ++h) {
+            const f32x4 v = {acc[4 * h], acc[4 * h + 1], acc[4 * h + 2], acc[4 * h + 3]};
+            store_out(d + h, v);
+        }
     }
 };
 
@@ -176,31 +205,54 @@ struct OutTraits<Bf16> {
     template <int VEC>
     __device__ __forceinline__ static void store(void* dst, const float (&acc)[VEC]) {
         if constexpr (VEC == 8) {
-            uint4 w;
-            w.x = pack_bf16x2(acc[0], acc[1]);
-            w.y = pack_bf16x2(acc[2], acc[3]);
-            w.z = pack_bf16x2(acc[4], acc[5]);
-            w.w = pack_bf16x2(acc[6], acc[7]);
-            *reinterpret_cast<uint4*>(dst) = w;
+            const u32x4 w = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                             pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
+            store_out(reinterpret_cast<u32x4*>(dst), w);
         } else {
-            uint2 w;
-            w.x = pack_bf16x2(acc[0], acc[1]);
-            w.y = pack_bf16x2(acc[2], acc[3]);
-            *reinterpret_cast<uint2*>(dst) = w;
+            const u32x2 w = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+            store_out(reinterpret_cast<u32x2*>(dst), w);
         }
     }
 };
 
+// Per-sample level geometry, read once per workgroup into LDS.
+struct LevelGeom {
+    int W, H, Z;            // level extents (Z = 1 in 2D)
+    uint32_t start_bytes;   // start pixel * row_bytes: the level's offset in an image
+};
+
+template <int DIM>
+__device__ __forceinline__ LevelGeom level_geom(const int64_t* shapes, const int64_t* starts,
+                                                int l, uint32_t row_bytes) {
+    LevelGeom g;
+    if (DIM == 2) {
+        g.W = static_cast<int>(shapes[2 * l + 1]);
+        g.H = static_cast<int>(shapes[2 * l + 0]);
+        g.Z = 1;
+    } else {
+        g.W = static_cast<int>(shapes[3 * l + 2]);
+        g.H = static_cast<int>(shapes[3 * l + 1]);
+        g.Z = static_cast<int>(shapes[3 * l + 0]);
+    }
+    g.start_bytes = static_cast<uint32_t>(starts[l]) * row_bytes;
+    return g;
+}
+
 // Phase A for one sample, branch-free.  xyz: normalized location; a: its
-// attention weight (0 for a dead lane); lm = (W, H, Z, start) of its level;
-// head_base: byte offset of (image n, pixel 0, head m) in the value slice.
+// attention weight; live: the lane holds a real sample; lg: its level.  The
+// corner at (k, i, j) of the level gets byte offset
+//   base + ((k*H + i)*W + j) * stride,
+// with base/stride addressing either the value tensor in HBM (base = image and
+// head offset + level start, stride = one pixel's M heads) or a copy of the
+// level in LDS (stride = one head row).  Corners outside the level get the
+// offset `invalid`, whose load reads zeros, and weight 0.
 template <int DIM>
 __device__ __forceinline__ Slot<DIM == 2 ? 4 : 8> make_slot(const float (&xyz)[DIM], float a,
-                                                            bool live, int4 lm,
-                                                            uint32_t head_base,
-                                                            uint32_t row_bytes) {
+                                                            bool live, const LevelGeom& lg,
+                                                            uint32_t base, uint32_t stride,
+                                                            uint32_t invalid) {
     constexpr int NC = DIM == 2 ? 4 : 8;
-    const int W = lm.x, H = lm.y, Z = lm.z;
+    const int W = lg.W, H = lg.H, Z = lg.Z;
     const float Wf = static_cast<float>(W), Hf = static_cast<float>(H);
     const float Zf = static_cast<float>(Z);
     // pixel-space coordinates: pixel j's centre is at normalized (j + 0.5) / W
@@ -226,14 +278,14 @@ __device__ __forceinline__ Slot<DIM == 2 ? 4 : 8> make_slot(const float (&xyz)[D
     const float wy[2] = {1.0f - fy, fy};
     const float wz[2] = {1.0f - fz, fz};
 
-    // byte offset of corner (z0, y0, x0); wraps for a corner at index -1, which
-    // is masked out (all offsets are exact modulo 2^32)
+    // offset of corner (z0, y0, x0); wraps for a corner at index -1, which is
+    // masked out (all offsets are exact modulo 2^32)
     const int zy = DIM == 3 ? z0 * H + y0 : y0;
-    const int pix = zy * W + x0 + lm.w;
-    const uint32_t o000 = static_cast<uint32_t>(pix) * row_bytes + head_base;
-    const uint32_t dx = row_bytes;
-    const uint32_t dy = static_cast<uint32_t>(W) * row_bytes;
-    const uint32_t dz = static_cast<uint32_t>(H * W) * row_bytes;
+    const int pix = zy * W + x0;
+    const uint32_t o000 = static_cast<uint32_t>(pix) * stride + base;
+    const uint32_t dx = stride;
+    const uint32_t dy = static_cast<uint32_t>(W) * stride;
+    const uint32_t dz = static_cast<uint32_t>(H * W) * stride;
 
     Slot<NC> sl;
 #pragma unroll
@@ -241,19 +293,125 @@ __device__ __forceinline__ Slot<DIM == 2 ? 4 : 8> make_slot(const float (&xyz)[D
         const int cx = k & 1, cy = (k >> 1) & 1, cz = k >> 2;
         const bool ok = inside && vx[cx] && vy[cy] && (DIM == 2 || vz[cz]);
         const float wzk = DIM == 3 ? wz[cz] : 1.0f;
-        sl.off[k] = ok ? o000 + (cz ? dz : 0u) + (cy ? dy : 0u) + (cx ? dx : 0u) : kOutOfRange;
+        sl.off[k] = ok ? o000 + (cz ? dz : 0u) + (cy ? dy : 0u) + (cx ? dx : 0u) : invalid;
         sl.w[k] = ok ? (aw * wzk) * (wy[cy] * wx[cx]) : 0.0f;
     }
     return sl;
 }
 
+// Location and weight of one sample, index sidx of this launch (0 if !live:
+// the loads then read zeros past the end of their buffers).
+template <int DIM>
+__device__ __forceinline__ void load_sample(const Params& p, bool live, uint32_t sidx,
+                                            float (&xyz)[DIM], float& a) {
+    const __amdgpu_buffer_rsrc_t rloc = buffer_of(p.loc, p.loc_bytes);
+    const __amdgpu_buffer_rsrc_t rattw = buffer_of(p.attw, p.attw_bytes);
+    const uint32_t loc_off = live ? sidx * (DIM * 4u) : kOutOfRange;
+    const uint32_t attw_off = live ? sidx * 4u : kOutOfRange;
+    if constexpr (DIM == 2) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(rloc, loc_off, 0, MSDA_STREAM_AUX);
+        xyz[0] = __uint_as_float(v[0]);
+        xyz[1] = __uint_as_float(v[1]);
+    } else {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b96(rloc, loc_off, 0, MSDA_STREAM_AUX);
+        xyz[0] = __uint_as_float(v[0]);
+        xyz[1] = __uint_as_float(v[1]);
+        xyz[2] = __uint_as_float(v[2]);
+    }
+    a = __uint_as_float(
+        __builtin_amdgcn_raw_buffer_load_b32(rattw, attw_off, 0, MSDA_STREAM_AUX));
+}
+
+template <typename TV, int NC, int VEC>
+__device__ __forceinline__ void fma_corners(const Slot<NC>& sl, const uint32_t (&raw)[NC][4],
+                                            float (&acc)[VEC]) {
+#pragma unroll
+    for (int k = 0; k < NC; ++k) {
+        float v[VEC];
+        ValueTraits<TV>::unpack(raw[k], v);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[e] = fmaf(sl.w[k], v[e], acc[e]);
+    }
+}
+
+// Phase B over slot iterations [i0, i1) whose corners live in the value
+// tensor: one 16-byte buffer load per corner.
+template <typename TV, int NC, int NG, int VEC>
+__device__ __forceinline__ void gather_hbm(__amdgpu_buffer_rsrc_t rsrc, const Slot<NC>* my,
+                                           int i0, int i1, uint32_t lane_off,
+                                           float (&acc)[VEC]) {
+#pragma unroll kGatherUnroll
+    for (int i = i0; i < i1; ++i) {
+        const Slot<NC> sl = my[i * NG];
+        uint32_t raw[NC][4];
+#pragma unroll
+        for (int k = 0; k < NC; ++k) {
+            const auto r = __builtin_amdgcn_raw_buffer_load_b128(rsrc, sl.off[k] + lane_off, 0, 0);
+            raw[k][0] = r[0];
+            raw[k][1] = r[1];
+            raw[k][2] = r[2];
+            raw[k][3] = r[3];
+        }
+        fma_corners<TV, NC, VEC>(sl, raw, acc);
+    }
+}
+
+// Phase B over slot iterations [i0, i1) whose corners were copied to LDS.
+template <typename TV, int NC, int NG, int VEC>
+__device__ __forceinline__ void gather_lds(const unsigned char* stage, const Slot<NC>* my,
+                                           int i0, int i1, uint32_t lane_off,
+                                           float (&acc)[VEC]) {
+#pragma unroll 4
+    for (int i = i0; i < i1; ++i) {
+        const Slot<NC> sl = my[i * NG];
+        uint32_t raw[NC][4];
+#pragma unroll
+        for (int k = 0; k < NC; ++k) {
+            const uint4 r = *reinterpret_cast<const uint4*>(stage + sl.off[k] + lane_off);
+            raw[k][0] = r.x;
+            raw[k][1] = r.y;
+            raw[k][2] = r.z;
+            raw[k][3] = r.w;
+        }
+        fma_corners<TV, NC, VEC>(sl, raw, acc);
+    }
+}
+
+// Sum the G point groups of each tile (lanes CPL apart) and store the lanes of
+// the first group.
+template <typename TO, int CPL, int VEC>
+__device__ __forceinline__ void reduce_store(float (&acc)[VEC], int G, bool store, void* out,
+                                             uint32_t row, uint32_t out_head_bytes, int c) {
+    for (int s = CPL; s < CPL * G; s <<= 1) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[e] += __shfl_xor(acc[e], s, kWave);
+    }
+    if (store) {
+        char* dst = static_cast<char*>(out) + static_cast<size_t>(row) * out_head_bytes +
+                    static_cast<size_t>(c) * (VEC * sizeof(TO));
+        OutTraits<TO>::template store<VEC>(dst, acc);
+    }
+}
+
+// Orders the LDS traffic of one wave: slot writes of phase A before the slot
+// reads of phase B, and those reads before the next chunk's writes.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ---------------------------------------------------------------------------
+// Direct kernel: one pass of T tiles per wave, every corner gathered from HBM
+// (through L2/L1).  Used for small problems and as the general path.
+// ---------------------------------------------------------------------------
 template <typename TV, typename TO, int DIM, int CPL>
 __global__ __launch_bounds__(kBlockThreads) void msda_forward_kernel(Params p) {
     constexpr int NC = DIM == 2 ? 4 : 8;     // corners per sample
     constexpr int NG = kWave / CPL;          // point groups per wave
     constexpr int VEC = ValueTraits<TV>::kVec;
 
-    __shared__ int4 smeta[kMaxSamplesPerTile];   // (W, H, Z, start) of sample s's level
+    __shared__ LevelGeom smeta[kMaxSamplesPerTile];   // level of sample s
     __shared__ Slot<NC> slots[kWavesPerBlock][kWave];
 
     const int tid = threadIdx.x;
@@ -262,18 +420,7 @@ __global__ __launch_bounds__(kBlockThreads) void msda_forward_kernel(Params p) {
 
     if (tid < p.LP) {
         const int l = static_cast<int>(fast_div(static_cast<uint32_t>(tid), p.div_P));
-        int4 lm;
-        if (DIM == 2) {
-            lm.x = static_cast<int>(p.shapes[2 * l + 1]);
-            lm.y = static_cast<int>(p.shapes[2 * l + 0]);
-            lm.z = 1;
-        } else {
-            lm.x = static_cast<int>(p.shapes[3 * l + 2]);
-            lm.y = static_cast<int>(p.shapes[3 * l + 1]);
-            lm.z = static_cast<int>(p.shapes[3 * l + 0]);
-        }
-        lm.w = static_cast<int>(p.starts[l]);
-        smeta[tid] = lm;
+        smeta[tid] = level_geom<DIM>(p.shapes, p.starts, l, p.row_bytes);
     }
 
     // wave -> slice (n, m) and first query q0, all wave-uniform
@@ -298,31 +445,16 @@ __global__ __launch_bounds__(kBlockThreads) void msda_forward_kernel(Params p) {
         const bool live = wave_live && i < p.NI && s < p.LP &&
                           q0 + static_cast<uint32_t>(t) < static_cast<uint32_t>(p.nq);
         const int s_c = live ? s : 0;
-        // sample index relative to row0 * LP
-        const uint32_t rel = static_cast<uint32_t>(t) * static_cast<uint32_t>(p.M * p.LP) +
-                             static_cast<uint32_t>(s_c);
-        const uint32_t sidx0 = row0 * static_cast<uint32_t>(p.LP);
-
-        const __amdgpu_buffer_rsrc_t rloc = buffer_of(p.loc, p.loc_bytes);
-        const __amdgpu_buffer_rsrc_t rattw = buffer_of(p.attw, p.attw_bytes);
-        const uint32_t loc_off = live ? (sidx0 + rel) * (DIM * 4u) : kOutOfRange;
-        const uint32_t attw_off = live ? (sidx0 + rel) * 4u : kOutOfRange;
-        float xyz[DIM];
-        if constexpr (DIM == 2) {
-            const auto v = __builtin_amdgcn_raw_buffer_load_b64(rloc, loc_off, 0, 0);
-            xyz[0] = __uint_as_float(v[0]);
-            xyz[1] = __uint_as_float(v[1]);
-        } else {
-            const auto v = __builtin_amdgcn_raw_buffer_load_b96(rloc, loc_off, 0, 0);
-            xyz[0] = __uint_as_float(v[0]);
-            xyz[1] = __uint_as_float(v[1]);
-            xyz[2] = __uint_as_float(v[2]);
-        }
-        const float a = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rattw, attw_off, 0, 0));
+        const uint32_t sidx = row0 * static_cast<uint32_t>(p.LP) +
+                              static_cast<uint32_t>(t) * static_cast<uint32_t>(p.M * p.LP) +
+                              static_cast<uint32_t>(s_c);
+        float xyz[DIM], a;
+        load_sample<DIM>(p, live, sidx, xyz, a);
 
         __syncthreads();  // smeta is ready
-        slots[wave][lane] =
-            make_slot<DIM>(xyz, a, live, smeta[s_c], head_base, p.row_bytes);
+        const LevelGeom lg = smeta[s_c];
+        slots[wave][lane] = make_slot<DIM>(xyz, a, live, lg, head_base + lg.start_bytes,
+                                           p.row_bytes, kOutOfRange);
     }
     __syncthreads();
 
@@ -332,46 +464,202 @@ __global__ __launch_bounds__(kBlockThreads) void msda_forward_kernel(Params p) {
     // lanes past the head's last chunk (D*size not a power-of-two multiple of
     // 16 bytes) re-read the last chunk and never store
     const uint32_t lane_off = static_cast<uint32_t>(min(c, p.nchunk - 1)) * 16u;
-    const __amdgpu_buffer_rsrc_t rsrc = buffer_of(p.value, p.value_bytes);
 
     float acc[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) acc[e] = 0.0f;
+    gather_hbm<TV, NC, NG, VEC>(buffer_of(p.value, p.value_bytes), &slots[wave][g], 0, p.NI,
+                                lane_off, acc);
 
-    const Slot<NC>* my = &slots[wave][g];
-#pragma unroll 4
-    for (int i = 0; i < p.NI; ++i) {
-        const Slot<NC> sl = my[i * NG];
-        uint32_t raw[NC][4];
-#pragma unroll
-        for (int k = 0; k < NC; ++k) {
-            const auto r = __builtin_amdgcn_raw_buffer_load_b128(rsrc, sl.off[k] + lane_off, 0, 0);
-            raw[k][0] = r[0];
-            raw[k][1] = r[1];
-            raw[k][2] = r[2];
-            raw[k][3] = r[3];
+    const bool store = j == 0 && c < p.nchunk && wave_live &&
+                       q0 + static_cast<uint32_t>(t) < static_cast<uint32_t>(p.nq);
+    reduce_store<TO, CPL, VEC>(acc, G, store, p.out, row0 + static_cast<uint32_t>(t * p.M),
+                               p.out_head_bytes, c);
+}
+
+// ---------------------------------------------------------------------------
+// Staged kernel.  A workgroup of kStagedWaves waves works on one (image, head)
+// slice, on every K-th chunk of kStagedWaves*T consecutive queries.  It first
+// copies into LDS that head's rows of the smallest levels that fit the LDS
+// budget (a level is copied whole), then loops over its chunks, T queries per
+// wave.  Samples of staged
+// levels are gathered from LDS, the others from HBM: the coarse levels, which
+// every query samples but which hold few pixels, then cost one HBM/L1 read per
+// row per workgroup instead of one per corner.  Phase-B iterations are ordered
+// HBM levels first, LDS levels last, so each of the two gather loops is
+// uniform across the wave.  Requires G to divide P (iterations never mix
+// levels).
+// ---------------------------------------------------------------------------
+constexpr int kStagedWaves = 16;
+constexpr int kStagedThreads = kStagedWaves * kWave;
+
+struct StagedParams {
+    Params p;
+    uint32_t wgs_per_slice;  // workgroups sharing one slice
+    FastDiv div_wgs;         // workgroup -> slice
+    uint32_t stage_bytes;    // dynamic LDS bytes: a zero row, then staged levels
+    int32_t ipl;             // phase-B iterations per level, P / G
+};
+
+template <typename TV, typename TO, int DIM, int CPL>
+__global__ __launch_bounds__(kStagedThreads) void msda_forward_staged_kernel(StagedParams sp) {
+    constexpr int NC = DIM == 2 ? 4 : 8;
+    constexpr int NG = kWave / CPL;
+    constexpr int VEC = ValueTraits<TV>::kVec;
+    const Params& p = sp.p;
+
+    extern __shared__ __align__(16) unsigned char stage[];
+    __shared__ LevelGeom smeta[kMaxSamplesPerTile];
+    __shared__ int lds_base_of[kMaxSamplesPerTile];   // staged level's LDS offset, or -1
+    __shared__ int iter_of[kMaxSamplesPerTile];       // phase-B iteration order
+    __shared__ LevelGeom lgeom[kMaxLevels];
+    __shared__ uint32_t lsize[kMaxLevels];
+    __shared__ int level_lds[kMaxLevels];
+    __shared__ int n_hbm_iters;
+    __shared__ Slot<NC> slots[kStagedWaves][kWave];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+
+    // workgroup -> slice (n, m) and its share of the slice's query chunks
+    // (kStagedWaves * T queries each): chunks k, k + K, k + 2K, ... for K
+    // workgroups per slice.  The K workgroups of a slice run side by side
+    // on one XCD, so at any time they cover K adjacent chunks: a narrow band of
+    // the slice whose value rows stay in that XCD's L2.
+    const uint32_t blk = xcd_contiguous_block(blockIdx.x, p.num_blocks);
+    const uint32_t slice = fast_div(blk, sp.div_wgs);
+    const uint32_t k_in_slice = blk - slice * sp.wgs_per_slice;
+    const uint32_t qb = static_cast<uint32_t>(p.nq);
+    const uint32_t n = fast_div(slice, p.div_M);
+    const uint32_t m = slice - n * static_cast<uint32_t>(p.M);
+    const uint32_t head_base = n * p.image_bytes + m * p.head_bytes;
+    const int G = 1 << p.log2G;
+
+    // ---- Which levels to stage: smallest first, while they fit.  Level l's
+    // offset is the zero row plus every smaller level (ties by index).
+    if (tid < p.L) {
+        lgeom[tid] = level_geom<DIM>(p.shapes, p.starts, tid, p.row_bytes);
+        lsize[tid] = static_cast<uint32_t>(lgeom[tid].W * lgeom[tid].H * lgeom[tid].Z);
+    }
+    if (tid < static_cast<int>(p.head_bytes / 16))
+        reinterpret_cast<uint4*>(stage)[tid] = make_uint4(0u, 0u, 0u, 0u);
+    __syncthreads();
+    if (tid < p.L) {
+        const uint32_t mine = lsize[tid];
+        uint64_t before = p.head_bytes;
+        for (int l = 0; l < p.L; ++l) {
+            const uint32_t other = lsize[l];
+            if (other < mine || (other == mine && l < tid))
+                before += static_cast<uint64_t>(other) * p.head_bytes;
         }
-#pragma unroll
-        for (int k = 0; k < NC; ++k) {
-            float v[VEC];
-            ValueTraits<TV>::unpack(raw[k], v);
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) acc[e] = fmaf(sl.w[k], v[e], acc[e]);
-        }
+        const uint64_t end = before + static_cast<uint64_t>(mine) * p.head_bytes;
+        level_lds[tid] = end <= sp.stage_bytes ? static_cast<int>(before) : -1;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int k = 0;
+        for (int l = 0; l < p.L; ++l)
+            if (level_lds[l] < 0)
+                for (int it = 0; it < sp.ipl; ++it) iter_of[k++] = l * sp.ipl + it;
+        n_hbm_iters = k;
+        for (int l = 0; l < p.L; ++l)
+            if (level_lds[l] >= 0)
+                for (int it = 0; it < sp.ipl; ++it) iter_of[k++] = l * sp.ipl + it;
+    }
+    if (tid < p.LP) {
+        const int l = static_cast<int>(fast_div(static_cast<uint32_t>(tid), p.div_P));
+        smeta[tid] = lgeom[l];
+        lds_base_of[tid] = level_lds[l];
     }
 
-    // Sum the G groups of each tile (lanes CPL apart, G <= NG).
-    for (int s = CPL; s < CPL * G; s <<= 1) {
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[e] += __shfl_xor(acc[e], s, kWave);
+    // ---- Copy the staged levels' rows of head m into LDS (rows of D values,
+    // CPL lanes per row, 16 bytes per lane).
+    const __amdgpu_buffer_rsrc_t rsrc = buffer_of(p.value, p.value_bytes);
+    {
+        const int g = tid / CPL, c = tid % CPL;
+        constexpr int kRowsPerPass = kStagedThreads / CPL;
+        for (int l = 0; l < p.L; ++l) {
+            const int base = level_lds[l];
+            if (base < 0) continue;
+            const LevelGeom lg = lgeom[l];
+            const int rows = static_cast<int>(lsize[l]);
+            for (int r0 = 0; r0 < rows; r0 += kRowsPerPass) {
+                const int r = r0 + g;
+                if (r < rows && c < p.nchunk) {
+                    const uint32_t src = head_base + lg.start_bytes +
+                                         static_cast<uint32_t>(r) * p.row_bytes +
+                                         static_cast<uint32_t>(c) * 16u;
+                    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, src, 0, 0);
+                    *reinterpret_cast<uint4*>(stage + base + r * p.head_bytes + c * 16) =
+                        make_uint4(v[0], v[1], v[2], v[3]);
+                }
+            }
+        }
     }
+    __syncthreads();
 
-    if (j == 0 && c < p.nchunk && wave_live &&
-        q0 + static_cast<uint32_t>(t) < static_cast<uint32_t>(p.nq)) {
-        const uint32_t row = row0 + static_cast<uint32_t>(t * p.M);
-        char* dst = static_cast<char*>(p.out) + static_cast<size_t>(row) * p.out_head_bytes +
-                    static_cast<size_t>(c) * (VEC * sizeof(TO));
-        OutTraits<TO>::template store<VEC>(dst, acc);
+    const int NI = p.NI;
+    const int ni_hbm = __builtin_amdgcn_readfirstlane(n_hbm_iters);
+    const int g = lane / CPL, c = lane % CPL;
+    const int tb = g >> p.log2G, jb = g & (G - 1);
+    const uint32_t lane_off = static_cast<uint32_t>(min(c, p.nchunk - 1)) * 16u;
+    // phase-A role of this lane: slot k = i'*NG + g' holds iteration iter_of[i']
+    const int ia = lane / NG, ga = lane % NG;
+    const int ta = ga >> p.log2G, ja = ga & (G - 1);
+    const int sa = ia < NI ? iter_of[ia] * G + ja : 0;
+    const LevelGeom lga = smeta[sa < p.LP ? sa : 0];
+    const int lds_a = lds_base_of[sa < p.LP ? sa : 0];
+    const uint32_t slot_base = lds_a >= 0 ? static_cast<uint32_t>(lds_a) : head_base + lga.start_bytes;
+    const uint32_t slot_stride = lds_a >= 0 ? p.head_bytes : p.row_bytes;
+    const uint32_t slot_invalid = lds_a >= 0 ? 0u : kOutOfRange;
+
+    const uint32_t span = static_cast<uint32_t>(kStagedWaves * p.T);
+    const uint32_t stride = span * sp.wgs_per_slice;   // queries between this WG's chunks
+    const uint32_t qa = k_in_slice * span;
+    const uint32_t lp = static_cast<uint32_t>(p.LP);
+    const uint32_t lane_rel = static_cast<uint32_t>(ta) * static_cast<uint32_t>(p.M * p.LP) +
+                              static_cast<uint32_t>(sa < p.LP ? sa : 0);
+    const bool lane_has_sample = ia < NI && sa < p.LP;
+
+    // Locations and weights of the first chunk; each later chunk's are loaded
+    // one chunk ahead.
+    uint32_t q0 = qa + static_cast<uint32_t>(wave * p.T);
+    float xyz[DIM], a;
+    bool live = lane_has_sample && q0 + static_cast<uint32_t>(ta) < qb;
+    load_sample<DIM>(p, live,
+                     ((n * static_cast<uint32_t>(p.Lq) + q0) * static_cast<uint32_t>(p.M) + m) * lp +
+                         lane_rel,
+                     xyz, a);
+    for (uint32_t qc = qa; qc < qb; qc += stride) {
+        const uint32_t row0 = (n * static_cast<uint32_t>(p.Lq) + q0) * static_cast<uint32_t>(p.M) + m;
+
+        // ---- Phase A
+        slots[wave][lane] = make_slot<DIM>(xyz, a, live, lga, slot_base, slot_stride, slot_invalid);
+        const uint32_t q_this = q0;
+        q0 += stride;
+        if (qc + stride < qb) {
+            live = lane_has_sample && q0 + static_cast<uint32_t>(ta) < qb;
+            load_sample<DIM>(
+                p, live,
+                ((n * static_cast<uint32_t>(p.Lq) + q0) * static_cast<uint32_t>(p.M) + m) * lp +
+                    lane_rel,
+                xyz, a);
+        }
+        wave_lds_sync();
+
+        // ---- Phase B
+        float acc[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[e] = 0.0f;
+        const Slot<NC>* my = &slots[wave][g];
+        gather_hbm<TV, NC, NG, VEC>(rsrc, my, 0, ni_hbm, lane_off, acc);
+        gather_lds<TV, NC, NG, VEC>(stage, my, ni_hbm, NI, lane_off, acc);
+
+        const bool store = jb == 0 && c < p.nchunk && q_this + static_cast<uint32_t>(tb) < qb;
+        reduce_store<TO, CPL, VEC>(acc, G, store, p.out, row0 + static_cast<uint32_t>(tb * p.M),
+                                   p.out_head_bytes, c);
+        wave_lds_sync();
     }
 }
 

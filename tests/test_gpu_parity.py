@@ -134,6 +134,40 @@ def test_small_cases(case, layout):
     run_case(inp, dims, "bf16")
 
 
+# Launches of >= 65536 (query, head) tiles whose point groups divide P run the
+# LDS-staged kernel; these shapes cover it: levels that fit the LDS budget or
+# not, fp32/bf16, D from 4 to 64 channels, 2D/3D, query counts that leave
+# ragged workgroups and waves.
+STAGED = [
+    # dims, dtype, N, shapes, Lq, M, D, P, layout
+    (2, "f32", 2, ((60, 90), (30, 45), (15, 23), (8, 12)), 7191, 8, 32, 4, "pixel_centres"),
+    (2, "f32", 2, ((60, 90), (30, 45), (15, 23), (8, 12)), 4103, 8, 32, 2, "random_refs"),
+    (2, "bf16", 2, ((60, 90), (30, 45), (15, 23), (8, 12)), 7191, 8, 32, 4, "pixel_centres"),
+    (2, "f32", 1, ((40, 40), (7, 9)), 9001, 8, 64, 4, "random_refs"),
+    (2, "f32", 3, ((50, 50), (3, 5)), 4099, 6, 8, 8, "uniform"),
+    (2, "f32", 1, ((300, 300),), 70001, 1, 4, 4, "uniform"),     # no level fits
+    (3, "f32", 2, ((16, 16, 16), (8, 8, 8), (4, 4, 4)), 4672, 8, 32, 4, "pixel_centres"),
+    (3, "bf16", 1, ((16, 16, 16), (8, 8, 8), (4, 4, 4)), 9000, 8, 32, 2, "random_refs"),
+]
+
+
+@pytest.mark.parametrize("case", STAGED, ids=lambda c: f"{c[0]}d-{c[1]}-N{c[2]}-L{len(c[3])}-Lq{c[4]}-M{c[5]}-D{c[6]}-P{c[7]}-{c[8]}")
+def test_staged_kernel_cases(case):
+    dims, dt, N, shapes, Lq, M, D, P, layout = case
+    S = sum(int(np.prod(sh)) for sh in shapes)
+    lq = None if layout == "pixel_centres" else Lq
+    if layout == "pixel_centres":
+        assert Lq == S
+    w = Workload("staged", dims, N, shapes, lq, M, D, P, dt, layout,
+                 0.05 if layout != "uniform" else 0.0, (-0.1, 1.1), 23)
+    assert w.N * w.queries_per_image * w.M >= 65536
+    _log(f"[staged] {case}")
+    inp = make_inputs(w)
+    run_case(inp, dims, "f32")
+    if dt == "bf16":
+        run_case(inp, dims, "bf16")
+
+
 def test_encoder_style_pixel_centre_queries():
     w = Workload("enc", 2, 2, ((20, 33), (10, 17), (5, 9), (3, 5)), None, 8, 32, 4,
                  "f32", "pixel_centres", 0.02, (0, 1), 9)
