@@ -13,13 +13,13 @@
 
 #include "msda_device.hpp"
 
-// Staged-kernel tuning (bytes of LDS for staged levels per workgroup, target
-// number of workgroups per launch, smallest launch worth staging).
+// Staged-kernel tuning (bytes of LDS for staged levels per workgroup,
+// workgroups sharing one (image, head) slice, smallest launch worth staging).
 #ifndef MSDA_STAGE_BUDGET
 #define MSDA_STAGE_BUDGET (34 * 1024 + 512)
 #endif
-#ifndef MSDA_STAGED_TARGET_WGS
-#define MSDA_STAGED_TARGET_WGS 2048
+#ifndef MSDA_STAGED_WGS_PER_SLICE
+#define MSDA_STAGED_WGS_PER_SLICE 128
 #endif
 #ifndef MSDA_STAGED_MIN_TILES
 #define MSDA_STAGED_MIN_TILES 65536
@@ -221,7 +221,7 @@ int forward(const void* value, int value_dtype, const int64_t* spatial_shapes,
             p.div_P = make_fast_div(static_cast<uint32_t>(P));
 
             // Staged kernel: large 2D launches whose phase-B iterations are
-            // level-pure (G divides P), with ~MSDA_STAGED_TARGET_WGS
+            // level-pure (G divides P), with MSDA_STAGED_WGS_PER_SLICE
             // workgroups splitting each slice's chunks of kStagedWaves * T
             // queries between them.  (3D pyramids' coarsest level is rarely
             // small enough to copy whole: 8^3 voxels of 32 fp32 channels are
@@ -231,9 +231,8 @@ int forward(const void* value, int value_dtype, const int64_t* spatial_shapes,
                 const int64_t pass = int64_t{msda::kStagedWaves} * T;
                 const int64_t slices = nbatch * M;
                 const int64_t chunks = (nquery + pass - 1) / pass;   // per slice
-                int64_t wgs_per_slice = (MSDA_STAGED_TARGET_WGS + slices - 1) / slices;
+                int64_t wgs_per_slice = MSDA_STAGED_WGS_PER_SLICE;
                 if (wgs_per_slice > chunks) wgs_per_slice = chunks;
-                if (wgs_per_slice < 1) wgs_per_slice = 1;
                 int64_t stage = (S + 1) * head_bytes;
                 if (stage > MSDA_STAGE_BUDGET) stage = MSDA_STAGE_BUDGET;
                 stage = stage / 16 * 16;
