@@ -10,7 +10,9 @@ never calls it and the two share no code.
 ``msda3d_oracle_forward`` take the same tensors as the GPU entry points (on
 the CPU), widen value and attention weights exactly to float64, keep the
 sampling locations in float32 (the precision of the corner-index decision),
-and return the float64 result ``[N, Lq, M*D]``.
+and return the float64 result ``[N, Lq, M*D]``.  ``msda_oracle_backward`` and
+``msda3d_oracle_backward`` return the float64 gradients with respect to value,
+sampling locations and attention weights for a given ``grad_out``.
 """
 from __future__ import annotations
 
@@ -49,6 +51,10 @@ def _load():
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [ptr] * 6 + [i64] * 7
+    for name in ("msda_oracle_backward", "msda3d_oracle_backward"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [ptr] * 9 + [i64] * 7
     _lib = lib
     return lib
 
@@ -95,6 +101,46 @@ def _run(dims, value, spatial_shapes, level_start_index, sampling_locations,
     if rc != 0:
         raise ValueError(f"oracle rejected its arguments (code {rc})")
     return out
+
+
+def _run_backward(dims, value, spatial_shapes, level_start_index, sampling_locations,
+                  attention_weights, grad_out):
+    lib = _load()
+    v = _as_numpy(value, np.float64)
+    shapes = _as_numpy(spatial_shapes, np.int64)
+    lsi = _as_numpy(level_start_index, np.int64)
+    loc = _as_numpy(sampling_locations, np.float32)
+    aw = _as_numpy(attention_weights, np.float64)
+    g = _as_numpy(grad_out, np.float64)
+    N, S, M, D = v.shape
+    _, Lq, _, L, P, _ = loc.shape
+    if g.shape != (N, Lq, M * D):
+        raise ValueError("grad_out must be [N, Lq, M*D]")
+    gv = np.empty_like(v)
+    gl = np.empty(loc.shape, dtype=np.float64)
+    ga = np.empty(aw.shape, dtype=np.float64)
+    fn = lib.msda_oracle_backward if dims == 2 else lib.msda3d_oracle_backward
+    rc = fn(v.ctypes.data, shapes.ctypes.data, lsi.ctypes.data, loc.ctypes.data,
+            aw.ctypes.data, g.ctypes.data, gv.ctypes.data, gl.ctypes.data, ga.ctypes.data,
+            N, S, M, D, Lq, L, P)
+    if rc != 0:
+        raise ValueError(f"oracle rejected its arguments (code {rc})")
+    return gv, gl, ga
+
+
+def msda_oracle_backward(value, spatial_shapes, level_start_index, sampling_locations,
+                         attention_weights, grad_out):
+    """2D backward: returns (grad_value, grad_sampling_locations,
+    grad_attention_weights), float64, shaped like value / locations / weights."""
+    return _run_backward(2, value, spatial_shapes, level_start_index, sampling_locations,
+                         attention_weights, grad_out)
+
+
+def msda3d_oracle_backward(value, spatial_shapes, level_start_index, sampling_locations,
+                           attention_weights, grad_out):
+    """3D backward (trilinear); see msda_oracle_backward."""
+    return _run_backward(3, value, spatial_shapes, level_start_index, sampling_locations,
+                         attention_weights, grad_out)
 
 
 def msda_oracle_forward(value, spatial_shapes, level_start_index,

@@ -183,3 +183,196 @@ int msda3d_oracle_forward(const double* value, const int64_t* spatial_shapes,
     }
     return 0;
 }
+
+/* Backward, 2D.  For each sample the forward is
+ *   contribution[d] = A * sum_c w_c * V_c[d],
+ *   w = {(1-fy)(1-fx), (1-fy)fx, fy(1-fx), fy fx} over corners (y0,x0),
+ *   (y0,x0+1), (y0+1,x0), (y0+1,x0+1),
+ * with V_c = 0 for a corner outside the level.  With g = grad_out[n][q][m][:]
+ * and dot_c = sum_d g[d] * V_c[d]:
+ *   dA      = sum_c w_c dot_c
+ *   dx      = A * W * ((1-fy)(dot_01 - dot_00) + fy (dot_11 - dot_10))
+ *   dy      = A * H * ((1-fx)(dot_10 - dot_00) + fx (dot_11 - dot_01))
+ *   dV_c[d] += A * w_c * g[d]          (in-range corners only)
+ * ("3D Attention That Knows Where to Look": gradients reach both the offsets
+ * and the weights; the chain rule through x_hat = x*W - 0.5 gives the W.) */
+int msda_oracle_backward(const double* value, const int64_t* spatial_shapes,
+                         const int64_t* level_start_index,
+                         const float* sampling_locations,
+                         const double* attention_weights, const double* grad_out,
+                         double* grad_value, double* grad_sampling_locations,
+                         double* grad_attention_weights,
+                         int64_t N, int64_t S, int64_t M, int64_t D,
+                         int64_t Lq, int64_t L, int64_t P) {
+    if (N < 0 || S < 0 || M < 0 || D < 0 || Lq < 0 || L < 0 || P < 0) return 2;
+    if (N == 0 || M == 0 || D == 0) return 0;
+    if (!value || !spatial_shapes || !level_start_index || !grad_value) return 1;
+    if (Lq > 0 && (!sampling_locations || !attention_weights || !grad_out ||
+                   !grad_sampling_locations || !grad_attention_weights))
+        return 1;
+    if (check_levels(spatial_shapes, level_start_index, L, S, 2)) return 2;
+
+    for (int64_t e = 0; e < N * S * M * D; ++e) grad_value[e] = 0.0;
+
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t q = 0; q < Lq; ++q) {
+            for (int64_t m = 0; m < M; ++m) {
+                const double* g = grad_out + ((n * Lq + q) * M + m) * D;
+                for (int64_t l = 0; l < L; ++l) {
+                    const int64_t H = spatial_shapes[2 * l + 0];
+                    const int64_t W = spatial_shapes[2 * l + 1];
+                    const int64_t start = level_start_index[l];
+                    for (int64_t p = 0; p < P; ++p) {
+                        const int64_t k = (((n * Lq + q) * M + m) * L + l) * P + p;
+                        const double a = attention_weights[k];
+                        const float xh = to_pixel(sampling_locations[2 * k + 0], W);
+                        const float yh = to_pixel(sampling_locations[2 * k + 1], H);
+                        grad_attention_weights[k] = 0.0;
+                        grad_sampling_locations[2 * k + 0] = 0.0;
+                        grad_sampling_locations[2 * k + 1] = 0.0;
+                        if (!in_support(xh, W) || !in_support(yh, H)) continue;
+
+                        const float x0f = floorf(xh);
+                        const float y0f = floorf(yh);
+                        const int64_t x0 = (int64_t)x0f;
+                        const int64_t y0 = (int64_t)y0f;
+                        const double fx = (double)xh - (double)x0f;
+                        const double fy = (double)yh - (double)y0f;
+
+                        double dot[2][2] = {{0.0, 0.0}, {0.0, 0.0}};
+                        double dA = 0.0;
+                        for (int dy = 0; dy < 2; ++dy) {
+                            const int64_t i = y0 + dy;
+                            const double wy = dy ? fy : 1.0 - fy;
+                            for (int dx = 0; dx < 2; ++dx) {
+                                const int64_t j = x0 + dx;
+                                const double wx = dx ? fx : 1.0 - fx;
+                                if (i < 0 || i >= H || j < 0 || j >= W) continue;
+                                const int64_t s = start + i * W + j;
+                                const double* v = value + ((n * S + s) * M + m) * D;
+                                double* gv = grad_value + ((n * S + s) * M + m) * D;
+                                double acc = 0.0;
+                                for (int64_t d = 0; d < D; ++d) {
+                                    acc += g[d] * v[d];
+                                    gv[d] += a * (wy * wx) * g[d];
+                                }
+                                dot[dy][dx] = acc;
+                                dA += (wy * wx) * acc;
+                            }
+                        }
+                        grad_attention_weights[k] = dA;
+                        grad_sampling_locations[2 * k + 0] =
+                            a * (double)W *
+                            ((1.0 - fy) * (dot[0][1] - dot[0][0]) + fy * (dot[1][1] - dot[1][0]));
+                        grad_sampling_locations[2 * k + 1] =
+                            a * (double)H *
+                            ((1.0 - fx) * (dot[1][0] - dot[0][0]) + fx * (dot[1][1] - dot[0][1]));
+                    }
+                }
+            }
+        }
+    }
+    return 0;
+}
+
+/* Backward, 3D: the same with 8 corners, weights wz*wy*wx and
+ *   dx = A * W * sum_{cz,cy} wz wy (dot_{cz,cy,1} - dot_{cz,cy,0}),
+ * likewise for y (H) and z (Z). */
+int msda3d_oracle_backward(const double* value, const int64_t* spatial_shapes,
+                           const int64_t* level_start_index,
+                           const float* sampling_locations,
+                           const double* attention_weights, const double* grad_out,
+                           double* grad_value, double* grad_sampling_locations,
+                           double* grad_attention_weights,
+                           int64_t N, int64_t S, int64_t M, int64_t D,
+                           int64_t Lq, int64_t L, int64_t P) {
+    if (N < 0 || S < 0 || M < 0 || D < 0 || Lq < 0 || L < 0 || P < 0) return 2;
+    if (N == 0 || M == 0 || D == 0) return 0;
+    if (!value || !spatial_shapes || !level_start_index || !grad_value) return 1;
+    if (Lq > 0 && (!sampling_locations || !attention_weights || !grad_out ||
+                   !grad_sampling_locations || !grad_attention_weights))
+        return 1;
+    if (check_levels(spatial_shapes, level_start_index, L, S, 3)) return 2;
+
+    for (int64_t e = 0; e < N * S * M * D; ++e) grad_value[e] = 0.0;
+
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t q = 0; q < Lq; ++q) {
+            for (int64_t m = 0; m < M; ++m) {
+                const double* g = grad_out + ((n * Lq + q) * M + m) * D;
+                for (int64_t l = 0; l < L; ++l) {
+                    const int64_t Z = spatial_shapes[3 * l + 0];
+                    const int64_t H = spatial_shapes[3 * l + 1];
+                    const int64_t W = spatial_shapes[3 * l + 2];
+                    const int64_t start = level_start_index[l];
+                    for (int64_t p = 0; p < P; ++p) {
+                        const int64_t k = (((n * Lq + q) * M + m) * L + l) * P + p;
+                        const double a = attention_weights[k];
+                        const float xh = to_pixel(sampling_locations[3 * k + 0], W);
+                        const float yh = to_pixel(sampling_locations[3 * k + 1], H);
+                        const float zh = to_pixel(sampling_locations[3 * k + 2], Z);
+                        grad_attention_weights[k] = 0.0;
+                        grad_sampling_locations[3 * k + 0] = 0.0;
+                        grad_sampling_locations[3 * k + 1] = 0.0;
+                        grad_sampling_locations[3 * k + 2] = 0.0;
+                        if (!in_support(xh, W) || !in_support(yh, H) || !in_support(zh, Z))
+                            continue;
+
+                        const float x0f = floorf(xh), y0f = floorf(yh), z0f = floorf(zh);
+                        const int64_t x0 = (int64_t)x0f, y0 = (int64_t)y0f, z0 = (int64_t)z0f;
+                        const double f[3] = {(double)xh - (double)x0f, (double)yh - (double)y0f,
+                                             (double)zh - (double)z0f};
+
+                        double dot[2][2][2] = {{{0.0, 0.0}, {0.0, 0.0}}, {{0.0, 0.0}, {0.0, 0.0}}};
+                        double dA = 0.0;
+                        for (int dz = 0; dz < 2; ++dz) {
+                            const int64_t kk = z0 + dz;
+                            const double wz = dz ? f[2] : 1.0 - f[2];
+                            for (int dy = 0; dy < 2; ++dy) {
+                                const int64_t i = y0 + dy;
+                                const double wy = dy ? f[1] : 1.0 - f[1];
+                                for (int dx = 0; dx < 2; ++dx) {
+                                    const int64_t j = x0 + dx;
+                                    const double wx = dx ? f[0] : 1.0 - f[0];
+                                    if (kk < 0 || kk >= Z || i < 0 || i >= H || j < 0 || j >= W)
+                                        continue;
+                                    const int64_t s = start + (kk * H + i) * W + j;
+                                    const double* v = value + ((n * S + s) * M + m) * D;
+                                    double* gv = grad_value + ((n * S + s) * M + m) * D;
+                                    const double w = wz * wy * wx;
+                                    double acc = 0.0;
+                                    for (int64_t d = 0; d < D; ++d) {
+                                        acc += g[d] * v[d];
+                                        gv[d] += a * w * g[d];
+                                    }
+                                    dot[dz][dy][dx] = acc;
+                                    dA += w * acc;
+                                }
+                            }
+                        }
+                        double gx = 0.0, gy = 0.0, gz = 0.0;
+                        for (int u = 0; u < 2; ++u) {
+                            for (int v2 = 0; v2 < 2; ++v2) {
+                                const double wz_u = u ? f[2] : 1.0 - f[2];
+                                const double wy_v = v2 ? f[1] : 1.0 - f[1];
+                                const double wx_v = v2 ? f[0] : 1.0 - f[0];
+                                const double wy_u = u ? f[1] : 1.0 - f[1];
+                                /* x: pairs differing in dx at (dz=u, dy=v2) */
+                                gx += wz_u * wy_v * (dot[u][v2][1] - dot[u][v2][0]);
+                                /* y: pairs differing in dy at (dz=u, dx=v2) */
+                                gy += wz_u * wx_v * (dot[u][1][v2] - dot[u][0][v2]);
+                                /* z: pairs differing in dz at (dy=u, dx=v2) */
+                                gz += wy_u * wx_v * (dot[1][u][v2] - dot[0][u][v2]);
+                            }
+                        }
+                        grad_attention_weights[k] = dA;
+                        grad_sampling_locations[3 * k + 0] = a * (double)W * gx;
+                        grad_sampling_locations[3 * k + 1] = a * (double)H * gy;
+                        grad_sampling_locations[3 * k + 2] = a * (double)Z * gz;
+                    }
+                }
+            }
+        }
+    }
+    return 0;
+}

@@ -75,6 +75,37 @@ int msda3d_oracle_forward(const double* value, const int64_t* spatial_shapes,
                           int64_t N, int64_t S, int64_t M, int64_t D,
                           int64_t Lq, int64_t L, int64_t P);
 
+/*
+ * Backward of the same core: given grad_out [N][Lq][M*D] (double), returns
+ *   grad_value              double [N][S][M][D]          (overwritten)
+ *   grad_sampling_locations double [N][Lq][M][L][P][dims] (overwritten)
+ *   grad_attention_weights  double [N][Lq][M][L][P]      (overwritten)
+ * The derivative of each sample follows its forward evaluation: the same
+ * fp32 pixel-space coordinate, the same corner cell (floor of it), so at an
+ * integer coordinate the derivative is the one of the cell to its right; a
+ * sample outside the support (forward contribution 0) has zero gradients.
+ *   d out / d A       = interp(value at the location)
+ *   d out / d x       = A * W * d interp / d fx   (fx = x_hat - floor(x_hat))
+ *   d out / d value_c = A * w_c  for each in-range corner c
+ */
+int msda_oracle_backward(const double* value, const int64_t* spatial_shapes,
+                         const int64_t* level_start_index,
+                         const float* sampling_locations,
+                         const double* attention_weights, const double* grad_out,
+                         double* grad_value, double* grad_sampling_locations,
+                         double* grad_attention_weights,
+                         int64_t N, int64_t S, int64_t M, int64_t D,
+                         int64_t Lq, int64_t L, int64_t P);
+
+int msda3d_oracle_backward(const double* value, const int64_t* spatial_shapes,
+                           const int64_t* level_start_index,
+                           const float* sampling_locations,
+                           const double* attention_weights, const double* grad_out,
+                           double* grad_value, double* grad_sampling_locations,
+                           double* grad_attention_weights,
+                           int64_t N, int64_t S, int64_t M, int64_t D,
+                           int64_t Lq, int64_t L, int64_t P);
+
 #ifdef __cplusplus
 }
 #endif
