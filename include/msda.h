@@ -116,6 +116,53 @@ int msda3d_forward(const void* value, int value_dtype,
                    int64_t N, int64_t S, int64_t M, int64_t D,
                    int64_t Lq, int64_t L, int64_t P, void* stream);
 
+/*
+ * 2D backward: gradients of a loss with respect to value, sampling_locations
+ * and attention_weights, given grad_out = d loss / d out [N][Lq][M*D]
+ * (grad_out_dtype).  Same inputs and conventions as msda_forward, and:
+ *   grad_value               float [N][S][M][D]          overwritten (zeroed,
+ *                            then accumulated with fp32 atomics: the order of
+ *                            additions, hence the last bits, may vary run to run)
+ *   grad_sampling_locations  float [N][Lq][M][L][P][2]   overwritten
+ *   grad_attention_weights   float [N][Lq][M][L][P]      overwritten
+ * The derivative of a sample follows its forward evaluation: same fp32
+ * pixel-space coordinate, same cell (the right-hand derivative at an integer
+ * coordinate); a sample outside the support has zero gradients.
+ *   d out / d A       = interp(value, location)
+ *   d out / d x       = A * W * d interp / d fx   (x_hat = x*W - 0.5)
+ *   d out / d value_c = A * w_c                    (in-range corners)
+ * The locations are reference point + offset ("3D Attention That Knows Where
+ * to Look", recipe steps 1-2; gradients "flow back into both the offsets and
+ * the weights"), so the location gradient is the offset gradient.
+ * Extra limits: one image's fp32 gradient S*M*D*4 < 2^31 bytes, and a bf16
+ * value image below 2^30 bytes (MSDA_ERR_OVERFLOW).  grad_value is 16-byte
+ * aligned; grad_out 16-byte aligned.  N == 0 is a no-op; Lq == 0 only zeroes
+ * grad_value.
+ */
+int msda_backward(const void* value, int value_dtype,
+                  const int64_t* spatial_shapes,
+                  const int64_t* level_start_index,
+                  const float* sampling_locations,
+                  const float* attention_weights,
+                  const void* grad_out, int grad_out_dtype,
+                  float* grad_value, float* grad_sampling_locations,
+                  float* grad_attention_weights,
+                  int64_t N, int64_t S, int64_t M, int64_t D,
+                  int64_t Lq, int64_t L, int64_t P, void* stream);
+
+/* 3D backward (trilinear); shapes [L][3], locations and their gradient
+ * [N][Lq][M][L][P][3]; otherwise as msda_backward. */
+int msda3d_backward(const void* value, int value_dtype,
+                    const int64_t* spatial_shapes,
+                    const int64_t* level_start_index,
+                    const float* sampling_locations,
+                    const float* attention_weights,
+                    const void* grad_out, int grad_out_dtype,
+                    float* grad_value, float* grad_sampling_locations,
+                    float* grad_attention_weights,
+                    int64_t N, int64_t S, int64_t M, int64_t D,
+                    int64_t Lq, int64_t L, int64_t P, void* stream);
+
 /* Static, human-readable description of a status code (never NULL). */
 const char* msda_status_string(int status);
 

@@ -11,7 +11,8 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libmsda.so")
 SOURCES = [os.path.join(CSRC, "msda_api.hip")]
-DEPENDS = SOURCES + [os.path.join(CSRC, "msda_device.hpp"), os.path.join(INCLUDE, "msda.h")]
+DEPENDS = SOURCES + [os.path.join(CSRC, "msda_device.hpp"), os.path.join(CSRC, "msda_backward.hpp"),
+                     os.path.join(INCLUDE, "msda.h")]
 
 ARCH = "gfx950"
 

@@ -1,9 +1,10 @@
 """Python binding of the C ABI in ``include/msda.h`` (argument marshalling only).
 
-``msda_forward`` and ``msda3d_forward`` take torch tensors that already live
-on the GPU, check dtypes/shapes/contiguity, allocate ``out`` with torch when
-the caller passes none, and call the same-named C entry point of
-``libmsda.so`` on torch's current HIP stream.  Every step of the computation
+``msda_forward`` / ``msda3d_forward`` and ``msda_backward`` /
+``msda3d_backward`` take torch tensors that already live on the GPU, check
+dtypes/shapes/contiguity, allocate outputs with torch when the caller passes
+none, and call the same-named C entry point of ``libmsda.so`` on torch's
+current HIP stream.  Every step of the computation
 runs in the library's kernels.  If ``libmsda.so`` has not been built, the
 first call raises; there is no fallback.
 """
@@ -32,7 +33,8 @@ STATUS = {
 }
 
 # Every symbol include/msda.h declares.
-EXPORTED = ("msda_forward", "msda3d_forward", "msda_status_string")
+EXPORTED = ("msda_forward", "msda3d_forward", "msda_backward", "msda3d_backward",
+            "msda_status_string")
 
 _lib = None
 
@@ -66,6 +68,11 @@ def load_library() -> ctypes.CDLL:
         fn.restype = ctypes.c_int
         fn.argtypes = [vp, ctypes.c_int, vp, vp, vp, vp, vp, ctypes.c_int,
                        i64, i64, i64, i64, i64, i64, i64, vp]
+    for name in ("msda_backward", "msda3d_backward"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [vp, ctypes.c_int, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp,
+                       i64, i64, i64, i64, i64, i64, i64, vp]
     lib.msda_status_string.restype = ctypes.c_char_p
     lib.msda_status_string.argtypes = [ctypes.c_int]
     _lib = lib
@@ -87,6 +94,19 @@ def raw_call(dims: int, value_ptr: int, value_dtype: int, shapes_ptr: int,
               out_ptr, out_dtype, N, S, M, D, Lq, L, P, stream)
 
 
+def raw_backward_call(dims: int, value_ptr: int, value_dtype: int, shapes_ptr: int,
+                      starts_ptr: int, loc_ptr: int, attw_ptr: int, grad_out_ptr: int,
+                      grad_out_dtype: int, grad_value_ptr: int, grad_loc_ptr: int,
+                      grad_attw_ptr: int, N: int, S: int, M: int, D: int, Lq: int, L: int,
+                      P: int, stream: int = 0) -> int:
+    """Call the backward C entry point with raw pointers; returns the msda_status."""
+    lib = load_library()
+    fn = lib.msda_backward if dims == 2 else lib.msda3d_backward
+    return fn(value_ptr, value_dtype, shapes_ptr, starts_ptr, loc_ptr, attw_ptr,
+              grad_out_ptr, grad_out_dtype, grad_value_ptr, grad_loc_ptr, grad_attw_ptr,
+              N, S, M, D, Lq, L, P, stream)
+
+
 def _dtype_code(dtype: torch.dtype, what: str) -> int:
     if dtype == torch.float32:
         return MSDA_F32
@@ -95,11 +115,9 @@ def _dtype_code(dtype: torch.dtype, what: str) -> int:
     raise TypeError(f"{what} must be float32 or bfloat16, got {dtype}")
 
 
-def _forward(dims: int, value: torch.Tensor, spatial_shapes: torch.Tensor,
-             level_start_index: torch.Tensor, sampling_locations: torch.Tensor,
-             attention_weights: torch.Tensor, out: Optional[torch.Tensor],
-             out_dtype: Optional[torch.dtype],
-             stream: Optional[torch.cuda.Stream]) -> torch.Tensor:
+def _check_inputs(dims, value, spatial_shapes, level_start_index, sampling_locations,
+                  attention_weights):
+    """Validate the forward inputs; returns (value dtype code, N, S, M, D, Lq, L, P)."""
     tensors = dict(value=value, spatial_shapes=spatial_shapes,
                    level_start_index=level_start_index,
                    sampling_locations=sampling_locations,
@@ -124,6 +142,16 @@ def _forward(dims: int, value: torch.Tensor, spatial_shapes: torch.Tensor,
         raise ValueError("sampling_locations / attention_weights do not match value")
     if spatial_shapes.shape != (L, dims) or level_start_index.shape != (L,):
         raise ValueError("spatial_shapes / level_start_index do not match L")
+    return code, N, S, M, D, Lq, L, P
+
+
+def _forward(dims: int, value: torch.Tensor, spatial_shapes: torch.Tensor,
+             level_start_index: torch.Tensor, sampling_locations: torch.Tensor,
+             attention_weights: torch.Tensor, out: Optional[torch.Tensor],
+             out_dtype: Optional[torch.dtype],
+             stream: Optional[torch.cuda.Stream]) -> torch.Tensor:
+    code, N, S, M, D, Lq, L, P = _check_inputs(dims, value, spatial_shapes, level_start_index,
+                                               sampling_locations, attention_weights)
     if out is None:
         dt = value.dtype if out_dtype is None else out_dtype
         out = torch.empty((N, Lq, M * D), dtype=dt, device=value.device)
@@ -159,3 +187,60 @@ def msda3d_forward(value, spatial_shapes, level_start_index, sampling_locations,
     [N,Lq,M,L,P,3] = (x, y, z); otherwise as ``msda_forward``."""
     return _forward(3, value, spatial_shapes, level_start_index, sampling_locations,
                     attention_weights, out, out_dtype, stream)
+
+
+def _backward(dims, value, spatial_shapes, level_start_index, sampling_locations,
+              attention_weights, grad_out, grad_value, grad_sampling_locations,
+              grad_attention_weights, stream):
+    code, N, S, M, D, Lq, L, P = _check_inputs(dims, value, spatial_shapes, level_start_index,
+                                               sampling_locations, attention_weights)
+    if not grad_out.is_cuda or not grad_out.is_contiguous() or grad_out.shape != (N, Lq, M * D):
+        raise ValueError("grad_out must be a contiguous [N, Lq, M*D] GPU tensor")
+    gcode = _dtype_code(grad_out.dtype, "grad_out")
+    dev = value.device
+
+    def _out(t, shape, name):
+        if t is None:
+            return torch.empty(shape, dtype=torch.float32, device=dev)
+        if (t.dtype != torch.float32 or tuple(t.shape) != tuple(shape)
+                or not t.is_contiguous() or t.device != dev):
+            raise ValueError(f"{name} must be a contiguous float32 {tuple(shape)} tensor")
+        return t
+
+    gv = _out(grad_value, (N, S, M, D), "grad_value")
+    gl = _out(grad_sampling_locations, tuple(sampling_locations.shape),
+              "grad_sampling_locations")
+    ga = _out(grad_attention_weights, tuple(attention_weights.shape), "grad_attention_weights")
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    status = raw_backward_call(dims, value.data_ptr(), code, spatial_shapes.data_ptr(),
+                               level_start_index.data_ptr(), sampling_locations.data_ptr(),
+                               attention_weights.data_ptr(), grad_out.data_ptr(), gcode,
+                               gv.data_ptr(), gl.data_ptr(), ga.data_ptr(),
+                               N, S, M, D, Lq, L, P, s.cuda_stream)
+    if status != 0:
+        raise MsdaError(status, status_string(status))
+    return gv, gl, ga
+
+
+def msda_backward(value, spatial_shapes, level_start_index, sampling_locations,
+                  attention_weights, grad_out, grad_value=None,
+                  grad_sampling_locations=None, grad_attention_weights=None,
+                  stream=None):
+    """2D MSDA backward: given ``grad_out`` [N, Lq, M*D] (fp32 or bf16) returns
+    float32 ``(grad_value [N,S,M,D], grad_sampling_locations [N,Lq,M,L,P,2],
+    grad_attention_weights [N,Lq,M,L,P])``; all three are overwritten (passed
+    tensors are reused).  grad_value is accumulated with fp32 atomics, so its
+    last bits may differ between runs.  Asynchronous on ``stream``."""
+    return _backward(2, value, spatial_shapes, level_start_index, sampling_locations,
+                     attention_weights, grad_out, grad_value, grad_sampling_locations,
+                     grad_attention_weights, stream)
+
+
+def msda3d_backward(value, spatial_shapes, level_start_index, sampling_locations,
+                    attention_weights, grad_out, grad_value=None,
+                    grad_sampling_locations=None, grad_attention_weights=None,
+                    stream=None):
+    """3D MSDA backward (trilinear); see ``msda_backward``."""
+    return _backward(3, value, spatial_shapes, level_start_index, sampling_locations,
+                     attention_weights, grad_out, grad_value, grad_sampling_locations,
+                     grad_attention_weights, stream)

@@ -1,0 +1,297 @@
+// Backward of the MSDA core for gfx950: gradients with respect to value,
+// sampling locations and attention weights.
+//
+// For one sample with attention weight A at pixel-space coordinate
+// (x_hat, y_hat) = (x*W - 0.5, y*H - 0.5), cell corner (x0, y0) = floor and
+// fractions (fx, fy), the forward adds A * sum_c w_c V_c with bilinear weights
+// w = {(1-fy)(1-fx), (1-fy)fx, fy(1-fx), fy fx} (zero for a corner outside the
+// level).  With g the output gradient of its (n, q, m) and dot_c = <g, V_c>:
+//   dA        = sum_c w_c dot_c
+//   dx        = A * W * ((1-fy)(dot_01 - dot_00) + fy (dot_11 - dot_10))
+//   dy        = A * H * ((1-fx)(dot_10 - dot_00) + fx (dot_11 - dot_01))
+//   dV_c     += A * w_c * g                          (scatter, fp32 atomics)
+// and the trilinear analogue in 3D ("3D Attention That Knows Where to Look":
+// gradients flow back into the offsets and the weights; the locations are
+// reference point + offset, so d/d offset = d/d location).
+//
+// Work decomposition: the forward's.  Phase A (one lane per sample) builds a
+// slot per sample in LDS; in phase B each lane loads its 16-byte chunk of the
+// value row of every corner, accumulates its share of dot_c, and adds its
+// chunk of A*w_c*g into grad_value with buffer atomics; the CPL lanes of a
+// group then sum the dot_c partials and the group's first lane writes the
+// sample's dA and dx (, dy, dz).
+#pragma once
+
+#include "msda_device.hpp"
+
+namespace msda {
+
+struct BwdParams {
+    Params f;                    // forward parameters of the same launch
+    const void* grad_out;        // at (n0, q0): rows of D gradients (grad dtype)
+    float* grad_value;           // this launch's images, [nb][S][M][D] fp32
+    float* grad_loc;             // at (n0, q0): like loc
+    float* grad_attw;            // at (n0, q0): like attw
+    uint32_t grad_value_bytes;   // byte size of this launch's grad_value slice
+    uint32_t grad_out_bytes;     // byte size of the grad_out rows this launch reads
+    uint32_t gout_head_bytes;    // D * sizeof(grad_out)
+    uint32_t value_shift;        // log2(4 / sizeof(value)): grad offset -> value offset
+};
+
+// Everything phase B needs about one sample.
+template <int NC, int DIM>
+struct __align__(16) BwdSlot {
+    uint32_t off[NC];   // byte offsets of the corner rows in grad_value (fp32)
+    float w[NC];        // pure interpolation weights (0 for corners outside)
+    float frac[DIM];    // fx, fy (, fz)
+    float ext[DIM];     // W, H (, Z) as floats: d x_hat / d x
+    float a;            // attention weight (0 for a dead or outside sample)
+    uint32_t sidx;      // sample index in this launch, or kNoSample
+};
+constexpr uint32_t kNoSample = 0xffffffffu;
+
+template <int DIM>
+__device__ __forceinline__ BwdSlot<DIM == 2 ? 4 : 8, DIM> make_bwd_slot(
+    const float (&xyz)[DIM], float a, bool live, uint32_t sidx, const LevelGeom& lg,
+    uint32_t base, uint32_t stride) {
+    constexpr int NC = DIM == 2 ? 4 : 8;
+    const int W = lg.W, H = lg.H, Z = lg.Z;
+    const float Wf = static_cast<float>(W), Hf = static_cast<float>(H);
+    const float Zf = static_cast<float>(Z);
+    const float xh = fmaf(xyz[0], Wf, -0.5f);
+    const float yh = fmaf(xyz[1], Hf, -0.5f);
+    const float zh = DIM == 3 ? fmaf(xyz[2], Zf, -0.5f) : 0.0f;
+    bool inside = live && xh > -1.0f && xh < Wf && yh > -1.0f && yh < Hf;
+    if (DIM == 3) inside = inside && zh > -1.0f && zh < Zf;
+
+    const float xs = inside ? xh : 0.0f, ys = inside ? yh : 0.0f, zs = inside ? zh : 0.0f;
+    const float x0f = floorf(xs), y0f = floorf(ys), z0f = floorf(zs);
+    const float fx = xs - x0f, fy = ys - y0f, fz = zs - z0f;
+    const int x0 = static_cast<int>(x0f), y0 = static_cast<int>(y0f);
+    const int z0 = static_cast<int>(z0f);
+    const bool vx[2] = {x0 >= 0, x0 + 1 < W};
+    const bool vy[2] = {y0 >= 0, y0 + 1 < H};
+    const bool vz[2] = {z0 >= 0, z0 + 1 < Z};
+    const float wx[2] = {1.0f - fx, fx};
+    const float wy[2] = {1.0f - fy, fy};
+    const float wz[2] = {1.0f - fz, fz};
+
+    const int zy = DIM == 3 ? z0 * H + y0 : y0;
+    const int pix = zy * W + x0;
+    const uint32_t o000 = static_cast<uint32_t>(pix) * stride + base;
+    const uint32_t dx = stride;
+    const uint32_t dy = static_cast<uint32_t>(W) * stride;
+    const uint32_t dz = static_cast<uint32_t>(H * W) * stride;
+
+    BwdSlot<NC, DIM> sl;
+#pragma unroll
+    for (int k = 0; k < NC; ++k) {
+        const int cx = k & 1, cy = (k >> 1) & 1, cz = k >> 2;
+        const bool ok = inside && vx[cx] && vy[cy] && (DIM == 2 || vz[cz]);
+        const float wzk = DIM == 3 ? wz[cz] : 1.0f;
+        sl.off[k] = ok ? o000 + (cz ? dz : 0u) + (cy ? dy : 0u) + (cx ? dx : 0u) : kOutOfRange;
+        sl.w[k] = ok ? wzk * (wy[cy] * wx[cx]) : 0.0f;
+    }
+    sl.frac[0] = fx;
+    sl.frac[1] = fy;
+    sl.ext[0] = Wf;
+    sl.ext[1] = Hf;
+    if constexpr (DIM == 3) {
+        sl.frac[2] = fz;
+        sl.ext[2] = Zf;
+    }
+    sl.a = inside ? a : 0.0f;
+    sl.sidx = live ? sidx : kNoSample;
+    return sl;
+}
+
+// Output-gradient chunk of VEC channels as fp32.
+template <typename TG, int VEC>
+__device__ __forceinline__ void load_grad(__amdgpu_buffer_rsrc_t r, uint32_t off, float (&g)[VEC]) {
+    if constexpr (sizeof(TG) == 4) {
+#pragma unroll
+        for (int h = 0; h < VEC / 4; ++h) {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16u * h, 0, MSDA_STREAM_AUX);
+            g[4 * h + 0] = __uint_as_float(v[0]);
+            g[4 * h + 1] = __uint_as_float(v[1]);
+            g[4 * h + 2] = __uint_as_float(v[2]);
+            g[4 * h + 3] = __uint_as_float(v[3]);
+        }
+    } else {
+        uint32_t raw[VEC / 2];
+        if constexpr (VEC == 8) {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, MSDA_STREAM_AUX);
+            raw[0] = v[0];
+            raw[1] = v[1];
+            raw[2] = v[2];
+            raw[3] = v[3];
+        } else {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, MSDA_STREAM_AUX);
+            raw[0] = v[0];
+            raw[1] = v[1];
+        }
+#pragma unroll
+        for (int e = 0; e < VEC / 2; ++e) {
+            g[2 * e] = __uint_as_float(raw[e] << 16);
+            g[2 * e + 1] = __uint_as_float(raw[e] & 0xffff0000u);
+        }
+    }
+}
+
+template <typename TV, typename TG, int DIM, int CPL>
+__global__ __launch_bounds__(kBlockThreads) void msda_backward_kernel(BwdParams bp) {
+    constexpr int NC = DIM == 2 ? 4 : 8;
+    constexpr int NG = kWave / CPL;
+    constexpr int VEC = ValueTraits<TV>::kVec;
+    const Params& p = bp.f;
+
+    __shared__ LevelGeom smeta[kMaxSamplesPerTile];
+    __shared__ BwdSlot<NC, DIM> slots[kWavesPerBlock][kWave];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+
+    // grad_value (fp32) geometry: one pixel row of all heads, one head row
+    const uint32_t ghead_bytes = p.head_bytes << bp.value_shift;
+    const uint32_t grow_bytes = static_cast<uint32_t>(p.M) * ghead_bytes;
+    const uint32_t gimage_bytes = p.image_bytes << bp.value_shift;
+    if (tid < p.LP) {
+        // level start in bytes of grad_value; value offsets follow by a shift
+        const int l = static_cast<int>(fast_div(static_cast<uint32_t>(tid), p.div_P));
+        smeta[tid] = level_geom<DIM>(p.shapes, p.starts, l, grow_bytes);
+    }
+
+    const uint32_t blk = xcd_contiguous_block(blockIdx.x, p.num_blocks);
+    const uint32_t wave_id =
+        __builtin_amdgcn_readfirstlane(blk * kWavesPerBlock + static_cast<uint32_t>(wave));
+    const bool wave_live = wave_id < p.waves;
+    const uint32_t slice = fast_div(wave_id, p.div_wps);
+    const uint32_t q0 = (wave_id - slice * p.wps) * static_cast<uint32_t>(p.T);
+    const uint32_t n = fast_div(slice, p.div_M);
+    const uint32_t m = slice - n * static_cast<uint32_t>(p.M);
+    const uint32_t row0 = (n * static_cast<uint32_t>(p.Lq) + q0) * static_cast<uint32_t>(p.M) + m;
+    const uint32_t ghead_base = n * gimage_bytes + m * ghead_bytes;
+    const int G = 1 << p.log2G;
+
+    // ---- Phase A: lane k fills slot k = i*NG + g.
+    {
+        const int i = lane / NG, g = lane % NG;
+        const int t = g >> p.log2G, j = g & (G - 1);
+        const int s = i * G + j;
+        const bool live = wave_live && i < p.NI && s < p.LP &&
+                          q0 + static_cast<uint32_t>(t) < static_cast<uint32_t>(p.nq);
+        const int s_c = live ? s : 0;
+        const uint32_t sidx = row0 * static_cast<uint32_t>(p.LP) +
+                              static_cast<uint32_t>(t) * static_cast<uint32_t>(p.M * p.LP) +
+                              static_cast<uint32_t>(s_c);
+        float xyz[DIM], a;
+        load_sample<DIM>(p, live, sidx, xyz, a);
+        __syncthreads();  // smeta is ready
+        const LevelGeom lg = smeta[s_c];
+        slots[wave][lane] =
+            make_bwd_slot<DIM>(xyz, a, live, sidx, lg, ghead_base + lg.start_bytes, grow_bytes);
+    }
+    __syncthreads();
+
+    // ---- Phase B
+    const int g = lane / CPL, c = lane % CPL;
+    const int t = g >> p.log2G;
+    const bool chunk_live = c < p.nchunk;
+    const uint32_t cc = static_cast<uint32_t>(min(c, p.nchunk - 1));
+    const uint32_t lane_off_v = cc * 16u;                    // in value
+    const uint32_t lane_off_g = lane_off_v << bp.value_shift;  // in grad_value
+    const __amdgpu_buffer_rsrc_t rval = buffer_of(p.value, p.value_bytes);
+    const __amdgpu_buffer_rsrc_t rgv = buffer_of(bp.grad_value, bp.grad_value_bytes);
+    const __amdgpu_buffer_rsrc_t rgo = buffer_of(bp.grad_out, bp.grad_out_bytes);
+
+    // this lane's VEC channels of the tile's output gradient (0 on idle lanes)
+    float gch[VEC];
+    {
+        const bool tile_live = wave_live && q0 + static_cast<uint32_t>(t) < static_cast<uint32_t>(p.nq);
+        const uint32_t row = row0 + static_cast<uint32_t>(t * p.M);
+        const uint32_t goff = tile_live && chunk_live
+                                  ? row * bp.gout_head_bytes + cc * (VEC * sizeof(TG))
+                                  : kOutOfRange;
+        load_grad<TG, VEC>(rgo, goff, gch);
+    }
+
+    const BwdSlot<NC, DIM>* my = &slots[wave][g];
+    for (int i = 0; i < p.NI; ++i) {
+        const BwdSlot<NC, DIM> sl = my[i * NG];
+        float dot[NC];
+#pragma unroll
+        for (int k = 0; k < NC; ++k) {
+            const uint32_t voff = sl.off[k] == kOutOfRange
+                                      ? kOutOfRange
+                                      : (sl.off[k] >> bp.value_shift) + lane_off_v;
+            const auto r = __builtin_amdgcn_raw_buffer_load_b128(rval, voff, 0, 0);
+            const uint32_t raw[4] = {r[0], r[1], r[2], r[3]};
+            float v[VEC];
+            ValueTraits<TV>::unpack(raw, v);
+            float d = 0.0f;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) d = fmaf(gch[e], v[e], d);
+            dot[k] = d;
+            if (sl.off[k] != kOutOfRange && chunk_live) {
+                const float aw = sl.a * sl.w[k];
+#pragma unroll
+                for (int e = 0; e < VEC; ++e)
+                    __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(
+                        aw * gch[e], rgv, sl.off[k] + lane_off_g + 4u * e, 0, 0);
+            }
+        }
+        // sum the CPL lanes' partial dots of this group
+#pragma unroll
+        for (int k = 0; k < NC; ++k)
+            for (int s = 1; s < CPL; s <<= 1) dot[k] += __shfl_xor(dot[k], s, kWave);
+
+        if (c == 0 && sl.sidx != kNoSample) {
+            float da = 0.0f;
+#pragma unroll
+            for (int k = 0; k < NC; ++k) da = fmaf(sl.w[k], dot[k], da);
+            float gl[DIM];
+            if constexpr (DIM == 2) {
+                const float fx = sl.frac[0], fy = sl.frac[1];
+                gl[0] = sl.a * sl.ext[0] *
+                        ((1.0f - fy) * (dot[1] - dot[0]) + fy * (dot[3] - dot[2]));
+                gl[1] = sl.a * sl.ext[1] *
+                        ((1.0f - fx) * (dot[2] - dot[0]) + fx * (dot[3] - dot[1]));
+            } else {
+                const float f[3] = {sl.frac[0], sl.frac[1], sl.frac[2]};
+                const float w0[3] = {1.0f - f[0], 1.0f - f[1], 1.0f - f[2]};
+                float g3[3] = {0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+#pragma unroll
+                    for (int v2 = 0; v2 < 2; ++v2) {
+                        // corner index k = cz*4 + cy*2 + cx
+                        const float wz_u = u ? f[2] : w0[2];
+                        const float wy_u = u ? f[1] : w0[1];
+                        const float wy_v = v2 ? f[1] : w0[1];
+                        const float wx_v = v2 ? f[0] : w0[0];
+                        g3[0] += wz_u * wy_v * (dot[u * 4 + v2 * 2 + 1] - dot[u * 4 + v2 * 2]);
+                        g3[1] += wz_u * wx_v * (dot[u * 4 + 2 + v2] - dot[u * 4 + v2]);
+                        g3[2] += wy_u * wx_v * (dot[4 + u * 2 + v2] - dot[u * 2 + v2]);
+                    }
+                }
+#pragma unroll
+                for (int d = 0; d < 3; ++d) gl[d] = sl.a * sl.ext[d] * g3[d];
+            }
+            // a sample outside the support has a = 0 and all weights 0: zeros
+            bp.grad_attw[sl.sidx] = da;
+#pragma unroll
+            for (int d = 0; d < DIM; ++d) bp.grad_loc[static_cast<size_t>(sl.sidx) * DIM + d] = gl[d];
+        }
+    }
+}
+
+// grad_value = 0 before the scatter (a plain fill kernel: no memset node in
+// a captured graph).
+__global__ __launch_bounds__(256) void msda_zero_kernel(float4* p, uint64_t n4) {
+    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * blockDim.x;
+    for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n4; i += stride)
+        p[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+}
+
+}  // namespace msda

@@ -1,4 +1,4 @@
-"""Seeded synthetic workloads for the MSDA forward core.
+"""Seeded synthetic workloads for the MSDA core (forward and backward).
 
 This module only draws inputs: it holds none of the sampling or interpolation
 arithmetic, and both the GPU path's tests/benchmark and the oracle consume
@@ -21,6 +21,8 @@ order):
      added to the reference point (float32);
   4. logits ~ N(0, 1) per (n, q, m, l, p); attention weights are their softmax
      over the L*P samples of each (n, q, m), taken in float64, stored float32.
+For a backward pass ``make_grad_out`` draws the output gradient ~ N(0, 1)
+from a generator of its own.
 """
 from __future__ import annotations
 
@@ -208,3 +210,23 @@ def make_inputs(w: Workload, seed: Optional[int] = None) -> Dict[str, torch.Tens
         "sampling_locations": loc,
         "attention_weights": attw,
     }
+
+
+def make_grad_out(w: Workload, dtype: Optional[str] = None,
+                  seed: Optional[int] = None) -> torch.Tensor:
+    """Draw the output gradient for a backward pass of workload ``w``.
+
+    ``grad_out`` ~ N(0, 1) as float32 [N, Lq, M*D] from its own generator
+    (seed: the workload's + 7919 unless given), rounded to bfloat16 (RNE) when
+    ``dtype`` is "bf16" (default: the workload's value dtype).
+    """
+    g = torch.Generator(device="cpu")
+    g.manual_seed(w.seed + 7919 if seed is None else seed)
+    grad = torch.randn((w.N, w.queries_per_image, w.M * w.D), generator=g,
+                       dtype=torch.float32)
+    dt = w.value_dtype if dtype is None else dtype
+    if dt == "bf16":
+        grad = grad.to(torch.bfloat16)
+    elif dt != "f32":
+        raise ValueError(f"unknown grad dtype {dt!r}")
+    return grad.contiguous()

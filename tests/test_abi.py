@@ -123,3 +123,43 @@ def test_binding_rejects_cpu_tensors(lib):
     with pytest.raises(ValueError):
         msda_forward(v, torch.tensor([[2, 2]]), torch.tensor([0]),
                      torch.zeros(1, 1, 1, 1, 1, 2), torch.ones(1, 1, 1, 1, 1))
+
+
+# ---- backward entry points (validation only: a call that passes every check
+# would launch the grad_value fill, so none is made here)
+
+def bcall(dims=2, value=A, dtype=0, shapes=A, starts=A, loc=A, attw=A, gout=A,
+          gout_dtype=0, gv=A, gl=A, ga=A, N=1, S=100, M=8, D=32, Lq=10, L=4, P=4):
+    return binding.raw_backward_call(dims, value, dtype, shapes, starts, loc, attw, gout,
+                                     gout_dtype, gv, gl, ga, N, S, M, D, Lq, L, P, 0)
+
+
+@pytest.mark.parametrize("dims", [2, 3])
+def test_backward_null_pointers(lib, dims):
+    for k in ("value", "shapes", "starts", "loc", "attw", "gout", "gv", "gl", "ga"):
+        assert bcall(dims, **{k: 0}) == NULL, k
+
+
+@pytest.mark.parametrize("dims", [2, 3])
+def test_backward_bad_dimensions_and_dtypes(lib, dims):
+    for k in ("N", "Lq"):
+        assert bcall(dims, **{k: -1}) == DIM
+    for k in ("S", "M", "D", "L", "P"):
+        assert bcall(dims, **{k: 0}) == DIM, k
+    assert bcall(dims, dtype=2) == DTYPE
+    assert bcall(dims, gout_dtype=-1) == DTYPE
+    # N == 0: nothing to do, even with null pointers
+    assert bcall(dims, N=0, value=0, gout=0, gv=0, gl=0, ga=0, loc=0, attw=0) == OK
+
+
+def test_backward_unsupported_misaligned_overflow(lib):
+    assert bcall(D=3) == UNSUP
+    assert bcall(D=4, dtype=1) == UNSUP
+    assert bcall(L=4, P=17) == UNSUP
+    assert bcall(gv=A + 4) == ALIGN
+    assert bcall(gout=A + 8) == ALIGN
+    assert bcall(gl=A + 2) == ALIGN
+    assert bcall(ga=A + 1) == ALIGN
+    # fp32 gradient image S*M*D*4 must stay below 2^31 bytes, also for bf16 value
+    assert bcall(S=(1 << 31) // (8 * 32 * 4), M=8, D=32, dtype=1) == OVERFLOW
+    assert bcall(M=1 << 31, D=4) == OVERFLOW

@@ -20,6 +20,7 @@ from scale_deformable_attention_02_amd import msda3d_forward, msda_forward
 from scale_deformable_attention_02_amd.workloads import (CONFIG_ORDER, CONFIGS,
                                                          Workload, level_starts,
                                                          make_inputs)
+from shape_cases import SMALL, STAGED
 
 pytestmark = pytest.mark.gpu
 
@@ -99,29 +100,8 @@ def test_encoder_bf16_value_with_bf16_output():
 
 
 # --------------------------------------------------------------------------
-# Small multi-tile cases with ragged tails over the launch-shape space:
-# D (chunks per head row 1..16, incl. non powers of two), L*P (1..64), dtype,
-# dims, batch, Lq not a multiple of any tile count.
+# Small multi-tile cases with ragged tails over the launch-shape space.
 # --------------------------------------------------------------------------
-SMALL = [
-    # dims, dtype, N, shapes, Lq, M, D, P
-    (2, "f32", 2, ((20, 33), (10, 17), (5, 9), (3, 5)), 301, 8, 32, 4),
-    (2, "bf16", 3, ((20, 33), (10, 17), (5, 9), (3, 5)), 257, 8, 32, 4),
-    (2, "f32", 1, ((16, 16),), 67, 2, 8, 4),
-    (2, "f32", 2, ((7, 9), (4, 5)), 33, 3, 4, 1),           # L*P = 2, D*4 = 16 B
-    (2, "f32", 1, ((7, 9),), 45, 5, 12, 1),                 # L*P = 1, 3 chunks
-    (2, "f32", 2, ((9, 11), (5, 6), (3, 3)), 29, 4, 64, 8),  # L*P = 24
-    (2, "bf16", 2, ((9, 11), (5, 6)), 41, 2, 24, 32),       # L*P = 64, 3 chunks
-    (2, "f32", 1, ((6, 10),) * 16, 13, 1, 128, 4),          # L = 16, L*P = 64
-    (2, "f32", 2, ((12, 7), (6, 4)), 50, 2, 256, 3),        # 64 chunks per row
-    (2, "bf16", 1, ((12, 7), (6, 4)), 50, 3, 512, 5),       # bf16, 64 chunks
-    (2, "f32", 3, ((5, 5), (3, 3), (2, 2)), 19, 6, 20, 5),  # L*P = 15, 5 chunks
-    (3, "f32", 2, ((8, 8, 8), (4, 4, 4), (2, 2, 2)), 219, 4, 32, 4),
-    (3, "bf16", 1, ((6, 7, 9), (3, 4, 5)), 111, 8, 32, 3),
-    (3, "f32", 1, ((3, 5, 7),), 37, 3, 8, 7),
-]
-
-
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: f"{c[0]}d-{c[1]}-N{c[2]}-L{len(c[3])}-Lq{c[4]}-M{c[5]}-D{c[6]}-P{c[7]}")
 @pytest.mark.parametrize("layout", ["uniform", "random_refs"])
 def test_small_cases(case, layout):
@@ -135,22 +115,7 @@ def test_small_cases(case, layout):
 
 
 # Launches of >= 65536 (query, head) tiles whose point groups divide P run the
-# LDS-staged kernel; these shapes cover it: levels that fit the LDS budget or
-# not, fp32/bf16, D from 4 to 64 channels, 2D/3D, query counts that leave
-# ragged workgroups and waves.
-STAGED = [
-    # dims, dtype, N, shapes, Lq, M, D, P, layout
-    (2, "f32", 2, ((60, 90), (30, 45), (15, 23), (8, 12)), 7191, 8, 32, 4, "pixel_centres"),
-    (2, "f32", 2, ((60, 90), (30, 45), (15, 23), (8, 12)), 4103, 8, 32, 2, "random_refs"),
-    (2, "bf16", 2, ((60, 90), (30, 45), (15, 23), (8, 12)), 7191, 8, 32, 4, "pixel_centres"),
-    (2, "f32", 1, ((40, 40), (7, 9)), 9001, 8, 64, 4, "random_refs"),
-    (2, "f32", 3, ((50, 50), (3, 5)), 4099, 6, 8, 8, "uniform"),
-    (2, "f32", 1, ((300, 300),), 70001, 1, 4, 4, "uniform"),     # no level fits
-    (3, "f32", 2, ((16, 16, 16), (8, 8, 8), (4, 4, 4)), 4672, 8, 32, 4, "pixel_centres"),
-    (3, "bf16", 1, ((16, 16, 16), (8, 8, 8), (4, 4, 4)), 9000, 8, 32, 2, "random_refs"),
-]
-
-
+# LDS-staged kernel.
 @pytest.mark.parametrize("case", STAGED, ids=lambda c: f"{c[0]}d-{c[1]}-N{c[2]}-L{len(c[3])}-Lq{c[4]}-M{c[5]}-D{c[6]}-P{c[7]}-{c[8]}")
 def test_staged_kernel_cases(case):
     dims, dt, N, shapes, Lq, M, D, P, layout = case
