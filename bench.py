@@ -3,10 +3,12 @@
 
 One step = one msda_forward call over one batch of the Deformable-DETR
 encoder workload (N=2, 4 levels (100,167),(50,84),(25,42),(13,21), S=Lq=22223,
-M=8, D=32, L=4, P=4, fp32), inputs already resident in HBM.  Steps cycle over
-several distinct copies of the inputs whose total exceeds twice the 256 MB
-Infinity Cache, so each step reads its inputs from HBM rather than from a
-cache warmed by the previous step.
+M=8, D=32, L=4, P=4, fp32), inputs already resident in HBM.  With
+``--op backward`` a step is one msda_backward call instead (grad_value fill
+plus the gradient kernel) on the same inputs and an N(0,1) output gradient.
+Steps cycle over several distinct copies of the inputs whose total exceeds
+twice the 256 MB Infinity Cache, so each step reads its inputs from HBM
+rather than from a cache warmed by the previous step.
 
 Prints one JSON line: sampled points/s over the timed steps, achieved
 effective HBM GB/s of the kernel against the 8 TB/s peak (roofline), the
@@ -29,18 +31,25 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "sampled points/sec + achieved HBM GB/s (DETR encoder shape, 1 MI355X)"
+METRIC_BACKWARD = ("backward sampled points/sec + achieved HBM GB/s "
+                   "(DETR encoder shape, 1 MI355X)")
 HBM_PEAK_GBPS = 8000.0
 MALL_BYTES = 256 << 20
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "msda_forward_counters.json")
-KERNEL_SOURCES = [
-    os.path.join(ROOT, "scale_deformable_attention_02_amd", "csrc", "msda_device.hpp"),
-    os.path.join(ROOT, "scale_deformable_attention_02_amd", "csrc", "msda_api.hip"),
-]
+CSRC = os.path.join(ROOT, "scale_deformable_attention_02_amd", "csrc")
+COUNTERS_FILES = {
+    "forward": os.path.join(ROOT, "profiles", "msda_forward_counters.json"),
+    "backward": os.path.join(ROOT, "profiles", "msda_backward_counters.json"),
+}
+KERNEL_SOURCES = {
+    "forward": [os.path.join(CSRC, "msda_device.hpp"), os.path.join(CSRC, "msda_api.hip")],
+    "backward": [os.path.join(CSRC, "msda_device.hpp"), os.path.join(CSRC, "msda_backward.hpp"),
+                 os.path.join(CSRC, "msda_api.hip")],
+}
 
 
-def kernel_source_digest() -> str:
+def kernel_source_digest(op: str = "forward") -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in KERNEL_SOURCES[op]:
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -65,13 +74,39 @@ def byte_counts(w):
     return U, G
 
 
-def counters_for(workload_name: str):
+def backward_byte_counts(w):
+    """Algorithmic bytes of one backward call (fill + gradient kernel).
+
+    U (compulsory): locations, weights, grad_out and value read once (value
+    capped at the gathered bytes), grad_locations, grad_weights and the fp32
+    grad_value written once.
+    G (gathered): every corner row of value read once per sample and every
+    corner row of grad_value updated once per sample (read-modify-write in
+    the L2 atomics: 2x its fp32 bytes), plus the streams.
+    """
+    samples = w.sampled_points
+    corners = 4 if w.dims == 2 else 8
+    loc = samples * w.dims * 4
+    attw = samples * 4
+    gout = w.N * w.queries_per_image * w.M * w.D * w.value_itemsize
+    value = w.N * w.S * w.M * w.D * w.value_itemsize
+    gvalue = w.N * w.S * w.M * w.D * 4
+    gathered_value = samples * corners * w.D * w.value_itemsize
+    scatter = samples * corners * w.D * 4
+    streams = 2 * (loc + attw) + gout
+    U = streams + min(value, gathered_value) + min(gvalue, scatter)
+    G = streams + gathered_value + 2 * scatter
+    return U, G
+
+
+def counters_for(workload_name: str, op: str = "forward"):
     """Per-launch HBM traffic from committed rocprofv3 counters, if current."""
-    if not os.path.exists(COUNTERS_FILE):
+    path = COUNTERS_FILES[op]
+    if not os.path.exists(path):
         return None
-    with open(COUNTERS_FILE) as f:
+    with open(path) as f:
         data = json.load(f)
-    if data.get("kernel_source_digest") != kernel_source_digest():
+    if data.get("kernel_source_digest") != kernel_source_digest(op):
         return None
     entry = data.get("workloads", {}).get(workload_name)
     if not entry:
@@ -79,13 +114,17 @@ def counters_for(workload_name: str):
     return entry.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(w, inp, max_points=60_000_000):
-    """Time the oracle (single-threaded C) on the same inputs, bounded."""
+def cpu_baseline(w, inp, max_points=60_000_000, grad_out=None):
+    """Time the oracle (single-threaded C) on the same inputs, bounded; the
+    backward oracle when ``grad_out`` is given."""
     import numpy as np
 
-    from oracle import msda3d_oracle_forward, msda_oracle_forward
+    import oracle
 
-    fn = msda_oracle_forward if w.dims == 2 else msda3d_oracle_forward
+    if grad_out is None:
+        fn = oracle.msda_oracle_forward if w.dims == 2 else oracle.msda3d_oracle_forward
+    else:
+        fn = oracle.msda_oracle_backward if w.dims == 2 else oracle.msda3d_oracle_backward
     per_query = w.M * w.L * w.P
     if w.sampled_points <= max_points:
         nb, nq = w.N, w.queries_per_image
@@ -98,8 +137,11 @@ def cpu_baseline(w, inp, max_points=60_000_000):
     attw = inp["attention_weights"][:nb, :nq].double().numpy()
     shapes = inp["spatial_shapes"].numpy()
     starts = inp["level_start_index"].numpy()
+    args = (value, shapes, starts, loc, attw)
+    if grad_out is not None:
+        args += (grad_out[:nb, :nq].double().numpy(),)
     t0 = time.perf_counter()
-    fn(value, shapes, starts, loc, attw)
+    fn(*args)
     dt = time.perf_counter() - t0
     points = nb * nq * per_query
     return {
@@ -119,6 +161,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="detr_encoder",
                     help="workload name (default: the DETR encoder configuration)")
+    ap.add_argument("--op", choices=("forward", "backward"), default="forward",
+                    help="time the forward (default) or the backward entry point")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip timing the oracle (for profiler runs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -134,25 +178,43 @@ def main(argv=None):
 
     import torch
 
-    from scale_deformable_attention_02_amd import msda3d_forward, msda_forward
-    from scale_deformable_attention_02_amd.workloads import CONFIGS, make_inputs
+    from scale_deformable_attention_02_amd import (msda3d_backward, msda3d_forward,
+                                                   msda_backward, msda_forward)
+    from scale_deformable_attention_02_amd.workloads import (CONFIGS, make_grad_out,
+                                                             make_inputs)
 
     w = CONFIGS[args.config]
     dev = torch.device("cuda:0")
     inp = make_inputs(w)
-    U, G = byte_counts(w)
+    backward = args.op == "backward"
+    U, G = backward_byte_counts(w) if backward else byte_counts(w)
     copies = max(2, -(-(2 * MALL_BYTES + 1) // U))
     base = {k: v.to(dev) for k, v in inp.items()}
+    if backward:
+        base["grad_out"] = make_grad_out(w).to(dev)
     sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(copies - 1)]
-    out_dt = torch.bfloat16 if w.out_dtype == "bf16" else torch.float32
-    outs = [torch.empty((w.N, w.queries_per_image, w.M * w.D), dtype=out_dt, device=dev)
-            for _ in range(copies)]
-    fwd = msda_forward if w.dims == 2 else msda3d_forward
+    if backward:
+        outs = [(torch.empty_like(d["value"], dtype=torch.float32),
+                 torch.empty_like(d["sampling_locations"]),
+                 torch.empty_like(d["attention_weights"])) for d in sets]
+        bwd = msda_backward if w.dims == 2 else msda3d_backward
 
-    def step(i):
-        d = sets[i % copies]
-        fwd(d["value"], d["spatial_shapes"], d["level_start_index"],
-            d["sampling_locations"], d["attention_weights"], out=outs[i % copies])
+        def step(i):
+            d = sets[i % copies]
+            gv, gl, ga = outs[i % copies]
+            bwd(d["value"], d["spatial_shapes"], d["level_start_index"],
+                d["sampling_locations"], d["attention_weights"], d["grad_out"],
+                grad_value=gv, grad_sampling_locations=gl, grad_attention_weights=ga)
+    else:
+        out_dt = torch.bfloat16 if w.out_dtype == "bf16" else torch.float32
+        outs = [torch.empty((w.N, w.queries_per_image, w.M * w.D), dtype=out_dt, device=dev)
+                for _ in range(copies)]
+        fwd = msda_forward if w.dims == 2 else msda3d_forward
+
+        def step(i):
+            d = sets[i % copies]
+            fwd(d["value"], d["spatial_shapes"], d["level_start_index"],
+                d["sampling_locations"], d["attention_weights"], out=outs[i % copies])
 
     for i in range(args.warmup):
         step(i)
@@ -194,9 +256,9 @@ def main(argv=None):
     points = w.sampled_points
     ms_per_step = wall / args.steps * 1e3
     achieved = U / kernel_s / 1e9
-    traffic = counters_for(w.name)
+    traffic = counters_for(w.name, args.op)
     result = {
-        "metric": METRIC,
+        "metric": METRIC_BACKWARD if backward else METRIC,
         "value": points / (wall / args.steps),
         "unit": "sampled points/s",
         "n_gpus": 1,
@@ -212,7 +274,7 @@ def main(argv=None):
             "workload": w.name, "N": w.N, "levels": [list(s) for s in w.shapes], "S": w.S,
             "Lq": w.queries_per_image, "M": w.M, "D": w.D, "L": w.L, "P": w.P,
             "value_dtype": w.value_dtype, "out_dtype": w.out_dtype,
-            "input_copies_cycled": copies,
+            "op": args.op, "input_copies_cycled": copies,
             "parallelism": "single GPU",
         },
         "achieved_hbm_gbps": achieved,
@@ -231,7 +293,8 @@ def main(argv=None):
         },
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, inp)
+        result["cpu_baseline"] = cpu_baseline(
+            w, inp, grad_out=make_grad_out(w) if backward else None)
     print(json.dumps(result), flush=True)
     return 0
 

@@ -418,6 +418,7 @@ int backward(const void* value, int value_dtype, const int64_t* spatial_shapes,
             bp.grad_out_bytes = static_cast<uint32_t>(nbatch * nquery * gout_per_query);
             bp.gout_head_bytes = static_cast<uint32_t>(gout_head_bytes);
             bp.value_shift = elem == 2 ? 1u : 0u;
+            bp.log2R = static_cast<uint32_t>(ceil_log2(D));
             launch_bwd<DIM>(value_dtype, grad_out_dtype, cpl, bp, hs);
             if (hipGetLastError() != hipSuccess) return MSDA_ERR_LAUNCH;
         }

@@ -15,11 +15,14 @@
 // reference point + offset, so d/d offset = d/d location).
 //
 // Work decomposition: the forward's.  Phase A (one lane per sample) builds a
-// slot per sample in LDS; in phase B each lane loads its 16-byte chunk of the
-// value row of every corner, accumulates its share of dot_c, and adds its
-// chunk of A*w_c*g into grad_value with buffer atomics; the CPL lanes of a
-// group then sum the dot_c partials and the group's first lane writes the
-// sample's dA and dx (, dy, dz).
+// slot per sample in LDS.  In phase B each lane loads its 16-byte chunk of the
+// value row of every corner and accumulates its share of dot_c; the CPL lanes
+// of a group then sum the dot_c partials and the group's first lane writes the
+// sample's dA and dx (, dy, dz).  Phase C scatters A*w_c*g into grad_value
+// with fp32 buffer atomics, lanes mapped to consecutive channels of a row so
+// that one instruction updates whole 64-byte sectors: the L2 retires about one
+// atomic request per sector, whatever the number of dwords in it, so a layout
+// with 8 dwords per 128-byte row per instruction runs 4x slower.
 #pragma once
 
 #include "msda_device.hpp"
@@ -36,7 +39,12 @@ struct BwdParams {
     uint32_t grad_out_bytes;     // byte size of the grad_out rows this launch reads
     uint32_t gout_head_bytes;    // D * sizeof(grad_out)
     uint32_t value_shift;        // log2(4 / sizeof(value)): grad offset -> value offset
+    uint32_t log2R;              // log2 of D rounded up to a power of two
 };
+
+// Output-gradient rows of one wave's tiles: T * D floats <= 64 * 16 / sizeof(value)
+// bytes / 4 (at most T * CPL * 16 bytes of value channels, 8 per chunk for bf16).
+constexpr int kGradTileFloats = 512;
 
 // Everything phase B needs about one sample.
 template <int NC, int DIM>
@@ -147,6 +155,7 @@ __global__ __launch_bounds__(kBlockThreads) void msda_backward_kernel(BwdParams 
 
     __shared__ LevelGeom smeta[kMaxSamplesPerTile];
     __shared__ BwdSlot<NC, DIM> slots[kWavesPerBlock][kWave];
+    __shared__ float gtile[kWavesPerBlock][kGradTileFloats];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -199,13 +208,14 @@ __global__ __launch_bounds__(kBlockThreads) void msda_backward_kernel(BwdParams 
     const int t = g >> p.log2G;
     const bool chunk_live = c < p.nchunk;
     const uint32_t cc = static_cast<uint32_t>(min(c, p.nchunk - 1));
-    const uint32_t lane_off_v = cc * 16u;                    // in value
-    const uint32_t lane_off_g = lane_off_v << bp.value_shift;  // in grad_value
+    const uint32_t lane_off_v = cc * 16u;  // in value
     const __amdgpu_buffer_rsrc_t rval = buffer_of(p.value, p.value_bytes);
     const __amdgpu_buffer_rsrc_t rgv = buffer_of(bp.grad_value, bp.grad_value_bytes);
     const __amdgpu_buffer_rsrc_t rgo = buffer_of(bp.grad_out, bp.grad_out_bytes);
 
-    // this lane's VEC channels of the tile's output gradient (0 on idle lanes)
+    // this lane's VEC channels of the tile's output gradient (0 on idle lanes);
+    // the first group of each tile also keeps the row in LDS for phase C
+    const int D = p.nchunk * VEC;
     float gch[VEC];
     {
         const bool tile_live = wave_live && q0 + static_cast<uint32_t>(t) < static_cast<uint32_t>(p.nq);
@@ -214,6 +224,10 @@ __global__ __launch_bounds__(kBlockThreads) void msda_backward_kernel(BwdParams 
                                   ? row * bp.gout_head_bytes + cc * (VEC * sizeof(TG))
                                   : kOutOfRange;
         load_grad<TG, VEC>(rgo, goff, gch);
+        if ((g & (G - 1)) == 0 && chunk_live) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) gtile[wave][t * D + c * VEC + e] = gch[e];
+        }
     }
 
     const BwdSlot<NC, DIM>* my = &slots[wave][g];
@@ -233,13 +247,6 @@ __global__ __launch_bounds__(kBlockThreads) void msda_backward_kernel(BwdParams 
 #pragma unroll
             for (int e = 0; e < VEC; ++e) d = fmaf(gch[e], v[e], d);
             dot[k] = d;
-            if (sl.off[k] != kOutOfRange && chunk_live) {
-                const float aw = sl.a * sl.w[k];
-#pragma unroll
-                for (int e = 0; e < VEC; ++e)
-                    __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(
-                        aw * gch[e], rgv, sl.off[k] + lane_off_g + 4u * e, 0, 0);
-            }
         }
         // sum the CPL lanes' partial dots of this group
 #pragma unroll
@@ -282,6 +289,31 @@ __global__ __launch_bounds__(kBlockThreads) void msda_backward_kernel(BwdParams 
             bp.grad_attw[sl.sidx] = da;
 #pragma unroll
             for (int d = 0; d < DIM; ++d) bp.grad_loc[static_cast<size_t>(sl.sidx) * DIM + d] = gl[d];
+        }
+    }
+
+    // ---- Phase C: grad_value[row_c][d] += A * w_c * g[t][d] over the flat
+    // index (slot, corner, channel padded to R); 64 / R rows per instruction
+    // (R <= 64), or a row in R / 64 instructions.  NG * R >= 128, so the trip
+    // count is the same on every lane.
+    wave_lds_sync();
+    constexpr int kLog2NC = DIM == 2 ? 2 : 3;
+    const uint32_t log2R = bp.log2R;
+    const uint32_t rmask = (1u << log2R) - 1u;
+    const uint32_t total = static_cast<uint32_t>(p.NI * NG) << (log2R + kLog2NC);
+    const int log2G = p.log2G;
+    for (uint32_t f = static_cast<uint32_t>(lane); f < total; f += kWave) {
+        const uint32_t d = f & rmask;
+        const uint32_t k = (f >> log2R) & (NC - 1);
+        const uint32_t sig = f >> (log2R + kLog2NC);
+        const BwdSlot<NC, DIM>* sp = &slots[wave][sig];
+        const uint32_t off = sp->off[k];
+        const float a = sp->a;
+        if (d < static_cast<uint32_t>(D) && off != kOutOfRange && a != 0.0f) {
+            const int ts = static_cast<int>(sig & (NG - 1)) >> log2G;
+            const float gd = gtile[wave][ts * D + static_cast<int>(d)];
+            __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(a * sp->w[k] * gd, rgv, off + 4u * d,
+                                                            0, 0);
         }
     }
 }
