@@ -5,7 +5,10 @@ One step = one msda_forward call over one batch of the Deformable-DETR
 encoder workload (N=2, 4 levels (100,167),(50,84),(25,42),(13,21), S=Lq=22223,
 M=8, D=32, L=4, P=4, fp32), inputs already resident in HBM.  With
 ``--op backward`` a step is one msda_backward call instead (grad_value fill
-plus the gradient kernel) on the same inputs and an N(0,1) output gradient.
+plus the gradient kernel) on the same inputs and an N(0,1) output gradient;
+with ``--op forward_fused`` one msda_forward_fused call on the same draws
+before the front end (reference points, offsets, logits), and the unfused
+pipeline (torch softmax + add, then msda_forward) is timed beside it.
 Steps cycle over several distinct copies of the inputs whose total exceeds
 twice the 256 MB Infinity Cache, so each step reads its inputs from HBM
 rather than from a cache warmed by the previous step.
@@ -33,15 +36,19 @@ if ROOT not in sys.path:
 METRIC = "sampled points/sec + achieved HBM GB/s (DETR encoder shape, 1 MI355X)"
 METRIC_BACKWARD = ("backward sampled points/sec + achieved HBM GB/s "
                    "(DETR encoder shape, 1 MI355X)")
+METRIC_FUSED = ("fused front end + forward sampled points/sec + achieved HBM GB/s "
+                "(DETR encoder shape, 1 MI355X)")
 HBM_PEAK_GBPS = 8000.0
 MALL_BYTES = 256 << 20
 CSRC = os.path.join(ROOT, "scale_deformable_attention_02_amd", "csrc")
 COUNTERS_FILES = {
     "forward": os.path.join(ROOT, "profiles", "msda_forward_counters.json"),
+    "forward_fused": os.path.join(ROOT, "profiles", "msda_forward_fused_counters.json"),
     "backward": os.path.join(ROOT, "profiles", "msda_backward_counters.json"),
 }
 KERNEL_SOURCES = {
     "forward": [os.path.join(CSRC, "msda_device.hpp"), os.path.join(CSRC, "msda_api.hip")],
+    "forward_fused": [os.path.join(CSRC, "msda_device.hpp"), os.path.join(CSRC, "msda_api.hip")],
     "backward": [os.path.join(CSRC, "msda_device.hpp"), os.path.join(CSRC, "msda_backward.hpp"),
                  os.path.join(CSRC, "msda_api.hip")],
 }
@@ -116,12 +123,17 @@ def counters_for(workload_name: str, op: str = "forward"):
 
 def cpu_baseline(w, inp, max_points=60_000_000, grad_out=None):
     """Time the oracle (single-threaded C) on the same inputs, bounded; the
-    backward oracle when ``grad_out`` is given."""
+    backward oracle when ``grad_out`` is given, the fused-front-end oracle when
+    ``inp`` holds reference points, offsets and logits."""
     import numpy as np
 
     import oracle
 
-    if grad_out is None:
+    fused = "reference_points" in inp
+    if fused:
+        fn = (oracle.msda_oracle_forward_fused if w.dims == 2
+              else oracle.msda3d_oracle_forward_fused)
+    elif grad_out is None:
         fn = oracle.msda_oracle_forward if w.dims == 2 else oracle.msda3d_oracle_forward
     else:
         fn = oracle.msda_oracle_backward if w.dims == 2 else oracle.msda3d_oracle_backward
@@ -133,11 +145,17 @@ def cpu_baseline(w, inp, max_points=60_000_000, grad_out=None):
         nb, nq = 1, max(1, max_points // per_query)
         sample = f"queries 0..{nq - 1} of image 0"
     value = inp["value"][:nb].double().numpy()
-    loc = np.ascontiguousarray(inp["sampling_locations"][:nb, :nq].numpy())
-    attw = inp["attention_weights"][:nb, :nq].double().numpy()
     shapes = inp["spatial_shapes"].numpy()
     starts = inp["level_start_index"].numpy()
-    args = (value, shapes, starts, loc, attw)
+    if fused:
+        args = (value, shapes, starts,
+                np.ascontiguousarray(inp["reference_points"][:nb, :nq].numpy()),
+                np.ascontiguousarray(inp["sampling_offsets"][:nb, :nq].numpy()),
+                inp["attention_logits"][:nb, :nq].double().numpy())
+    else:
+        loc = np.ascontiguousarray(inp["sampling_locations"][:nb, :nq].numpy())
+        attw = inp["attention_weights"][:nb, :nq].double().numpy()
+        args = (value, shapes, starts, loc, attw)
     if grad_out is not None:
         args += (grad_out[:nb, :nq].double().numpy(),)
     t0 = time.perf_counter()
@@ -161,8 +179,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="detr_encoder",
                     help="workload name (default: the DETR encoder configuration)")
-    ap.add_argument("--op", choices=("forward", "backward"), default="forward",
-                    help="time the forward (default) or the backward entry point")
+    ap.add_argument("--op", choices=("forward", "forward_fused", "backward"), default="forward",
+                    help="time the forward (default), the forward with the fused front "
+                         "end, or the backward entry point")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip timing the oracle (for profiler runs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -179,15 +198,20 @@ def main(argv=None):
     import torch
 
     from scale_deformable_attention_02_amd import (msda3d_backward, msda3d_forward,
-                                                   msda_backward, msda_forward)
-    from scale_deformable_attention_02_amd.workloads import (CONFIGS, make_grad_out,
-                                                             make_inputs)
+                                                   msda3d_forward_fused, msda_backward,
+                                                   msda_forward, msda_forward_fused)
+    from scale_deformable_attention_02_amd.workloads import (CONFIGS, make_fused_inputs,
+                                                             make_grad_out, make_inputs)
 
     w = CONFIGS[args.config]
     dev = torch.device("cuda:0")
-    inp = make_inputs(w)
     backward = args.op == "backward"
+    fused = args.op == "forward_fused"
+    inp = make_fused_inputs(w) if fused else make_inputs(w)
     U, G = backward_byte_counts(w) if backward else byte_counts(w)
+    if fused:  # plus the reference points, read once
+        U += w.N * w.queries_per_image * w.dims * 4
+        G += w.N * w.queries_per_image * w.dims * 4
     copies = max(2, -(-(2 * MALL_BYTES + 1) // U))
     base = {k: v.to(dev) for k, v in inp.items()}
     if backward:
@@ -205,6 +229,25 @@ def main(argv=None):
             bwd(d["value"], d["spatial_shapes"], d["level_start_index"],
                 d["sampling_locations"], d["attention_weights"], d["grad_out"],
                 grad_value=gv, grad_sampling_locations=gl, grad_attention_weights=ga)
+    elif fused:
+        out_dt = torch.bfloat16 if w.out_dtype == "bf16" else torch.float32
+        outs = [torch.empty((w.N, w.queries_per_image, w.M * w.D), dtype=out_dt, device=dev)
+                for _ in range(copies)]
+        ffn = msda_forward_fused if w.dims == 2 else msda3d_forward_fused
+        fwd = msda_forward if w.dims == 2 else msda3d_forward
+
+        def step(i):
+            d = sets[i % copies]
+            ffn(d["value"], d["spatial_shapes"], d["level_start_index"], d["reference_points"],
+                d["sampling_offsets"], d["attention_logits"], out=outs[i % copies])
+
+        def unfused_step(i):
+            d = sets[i % copies]
+            N, Lq, M, L, P, dims = d["sampling_offsets"].shape
+            loc = d["reference_points"].reshape(N, Lq, 1, 1, 1, dims) + d["sampling_offsets"]
+            attw = torch.softmax(d["attention_logits"].reshape(N, Lq, M, L * P), dim=-1)
+            fwd(d["value"], d["spatial_shapes"], d["level_start_index"], loc,
+                attw.reshape(N, Lq, M, L, P), out=outs[i % copies])
     else:
         out_dt = torch.bfloat16 if w.out_dtype == "bf16" else torch.float32
         outs = [torch.empty((w.N, w.queries_per_image, w.M * w.D), dtype=out_dt, device=dev)
@@ -244,6 +287,18 @@ def main(argv=None):
     torch.cuda.synchronize()
     warm_s = statistics.median([a.elapsed_time(b) for a, b in warm_ev]) / 1e3
 
+    unfused_us = None
+    if fused:
+        # the same work with the front end as separate torch passes
+        for i in range(3):
+            unfused_step(i)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for i in range(args.steps):
+            unfused_step(i)
+        torch.cuda.synchronize()
+        unfused_us = (time.perf_counter() - t1) / args.steps * 1e6
+
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
@@ -258,7 +313,7 @@ def main(argv=None):
     achieved = U / kernel_s / 1e9
     traffic = counters_for(w.name, args.op)
     result = {
-        "metric": METRIC_BACKWARD if backward else METRIC,
+        "metric": METRIC_BACKWARD if backward else (METRIC_FUSED if fused else METRIC),
         "value": points / (wall / args.steps),
         "unit": "sampled points/s",
         "n_gpus": 1,
@@ -283,6 +338,7 @@ def main(argv=None):
         "kernel_us_median": statistics.median(launch_ms) * 1e3,
         "kernel_us_warm_median": warm_s * 1e6,
         "bytes_per_launch": {"compulsory": U, "gathered": G},
+        "unfused_pipeline_us_per_step": unfused_us,
         "roofline": {
             "bound": "hbm",
             "achieved": achieved,

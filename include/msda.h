@@ -117,6 +117,42 @@ int msda3d_forward(const void* value, int value_dtype,
                    int64_t Lq, int64_t L, int64_t P, void* stream);
 
 /*
+ * 2D forward with the module's front end fused into the kernel.  Instead of
+ * sampling_locations and attention_weights it takes
+ *   reference_points   float [N][Lq][2]            (x, y), normalized
+ *   sampling_offsets   float [N][Lq][M][L][P][2]   normalized units
+ *   attention_logits   float [N][Lq][M][L][P]
+ * and samples at location = reference point + offset (one fp32 addition per
+ * coordinate: "3D Attention That Knows Where to Look", recipe steps 1-2) with
+ * attention weight A = softmax of the logits over the L*P samples of each
+ * (n, q, m) ("Deformable Attention Module": weights over the sampled keys
+ * sum to 1; "3D Attention...": predicted weights are softmaxed, one sum over
+ * L x P).  The softmax runs in fp32 (maximum subtracted, expf); non-finite
+ * logits give undefined (NaN) outputs.  Everything else, including limits,
+ * alignment (reference_points 4-byte aligned) and errors, is msda_forward's.
+ */
+int msda_forward_fused(const void* value, int value_dtype,
+                       const int64_t* spatial_shapes,
+                       const int64_t* level_start_index,
+                       const float* reference_points,
+                       const float* sampling_offsets,
+                       const float* attention_logits,
+                       void* out, int out_dtype,
+                       int64_t N, int64_t S, int64_t M, int64_t D,
+                       int64_t Lq, int64_t L, int64_t P, void* stream);
+
+/* 3D counterpart: reference_points [N][Lq][3], offsets [...][3]. */
+int msda3d_forward_fused(const void* value, int value_dtype,
+                         const int64_t* spatial_shapes,
+                         const int64_t* level_start_index,
+                         const float* reference_points,
+                         const float* sampling_offsets,
+                         const float* attention_logits,
+                         void* out, int out_dtype,
+                         int64_t N, int64_t S, int64_t M, int64_t D,
+                         int64_t Lq, int64_t L, int64_t P, void* stream);
+
+/*
  * 2D backward: gradients of a loss with respect to value, sampling_locations
  * and attention_weights, given grad_out = d loss / d out [N][Lq][M*D]
  * (grad_out_dtype).  Same inputs and conventions as msda_forward, and:

@@ -13,6 +13,9 @@ sampling locations in float32 (the precision of the corner-index decision),
 and return the float64 result ``[N, Lq, M*D]``.  ``msda_oracle_backward`` and
 ``msda3d_oracle_backward`` return the float64 gradients with respect to value,
 sampling locations and attention weights for a given ``grad_out``.
+``msda_oracle_forward_fused`` and ``msda3d_oracle_forward_fused`` add the
+module's front end: softmax of attention logits (fp64) and location =
+reference point + offset (fp32), then the same forward.
 """
 from __future__ import annotations
 
@@ -55,6 +58,10 @@ def _load():
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [ptr] * 9 + [i64] * 7
+    for name in ("msda_oracle_forward_fused", "msda3d_oracle_forward_fused"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [ptr] * 7 + [i64] * 7
     _lib = lib
     return lib
 
@@ -155,3 +162,43 @@ def msda3d_oracle_forward(value, spatial_shapes, level_start_index,
     """3D oracle: value [N,S,M,D], shapes [L,3]=(Z,H,W), locations [...,3]."""
     return _run(3, value, spatial_shapes, level_start_index, sampling_locations,
                 attention_weights)
+
+
+def _run_fused(dims, value, spatial_shapes, level_start_index, reference_points,
+               sampling_offsets, attention_logits):
+    lib = _load()
+    v = _as_numpy(value, np.float64)
+    shapes = _as_numpy(spatial_shapes, np.int64)
+    lsi = _as_numpy(level_start_index, np.int64)
+    ref = _as_numpy(reference_points, np.float32)
+    off = _as_numpy(sampling_offsets, np.float32)
+    z = _as_numpy(attention_logits, np.float64)
+    N, S, M, D = v.shape
+    if off.ndim != 6 or off.shape[-1] != dims:
+        raise ValueError(f"sampling_offsets must be [N, Lq, M, L, P, {dims}]")
+    _, Lq, _, L, P, _ = off.shape
+    if ref.shape != (N, Lq, dims) or z.shape != off.shape[:-1]:
+        raise ValueError("inconsistent shapes")
+    out = np.empty((N, Lq, M * D), dtype=np.float64)
+    fn = lib.msda_oracle_forward_fused if dims == 2 else lib.msda3d_oracle_forward_fused
+    rc = fn(v.ctypes.data, shapes.ctypes.data, lsi.ctypes.data, ref.ctypes.data,
+            off.ctypes.data, z.ctypes.data, out.ctypes.data, N, S, M, D, Lq, L, P)
+    if rc != 0:
+        raise ValueError(f"oracle rejected its arguments (code {rc})")
+    return out
+
+
+def msda_oracle_forward_fused(value, spatial_shapes, level_start_index, reference_points,
+                              sampling_offsets, attention_logits) -> np.ndarray:
+    """2D forward with the front end: reference_points [N,Lq,2], offsets
+    [N,Lq,M,L,P,2], logits [N,Lq,M,L,P]; returns float64 [N, Lq, M*D]."""
+    return _run_fused(2, value, spatial_shapes, level_start_index, reference_points,
+                      sampling_offsets, attention_logits)
+
+
+def msda3d_oracle_forward_fused(value, spatial_shapes, level_start_index, reference_points,
+                                sampling_offsets, attention_logits) -> np.ndarray:
+    """3D forward with the front end (reference points and offsets have 3
+    components)."""
+    return _run_fused(3, value, spatial_shapes, level_start_index, reference_points,
+                      sampling_offsets, attention_logits)

@@ -9,6 +9,7 @@
 
 #include <math.h>
 #include <stddef.h>
+#include <stdlib.h>
 
 /* Pixel-space coordinate of a normalized location along an axis of `extent`
  * pixels: pixel j's centre sits at (j + 0.5) / extent, so x_hat = x*extent -
@@ -375,4 +376,79 @@ int msda3d_oracle_backward(const double* value, const int64_t* spatial_shapes,
         }
     }
     return 0;
+}
+
+/* Front end of the module, then the core above.  The attention weights are a
+ * softmax of the predicted logits over the L*P samples of each (n, q, m):
+ * "Deformable Attention Module" normalises A over the sampled keys to sum to
+ * 1, "What is Deformable Attention" takes a softmax over only those keys, and
+ * "3D Attention That Knows Where to Look" predicts the weights with a linear
+ * layer, softmaxes them, and makes one sum over L x P samples.  Each sampling
+ * location is the query's normalized reference point plus the predicted
+ * offset ("3D Attention...", recipe steps 1-2), one per (n, q), shared by
+ * every head, level and point.  The softmax is evaluated in fp64 with the
+ * maximum subtracted; the location is one fp32 addition, since the location
+ * then decides a corner index in fp32 on both sides. */
+static int forward_fused(int dims, const double* value, const int64_t* spatial_shapes,
+                         const int64_t* level_start_index, const float* reference_points,
+                         const float* sampling_offsets, const double* attention_logits,
+                         double* out, int64_t N, int64_t S, int64_t M, int64_t D,
+                         int64_t Lq, int64_t L, int64_t P) {
+    if (N < 0 || Lq < 0 || S < 1 || M < 1 || D < 1 || L < 1 || P < 1) return 2;
+    if (N == 0 || Lq == 0) return 0;
+    if (!reference_points || !sampling_offsets || !attention_logits) return 1;
+    const int64_t LP = L * P;
+    const int64_t rows = N * Lq * M;
+    float* loc = malloc(sizeof(float) * (size_t)(rows * LP * dims));
+    double* attw = malloc(sizeof(double) * (size_t)(rows * LP));
+    if (!loc || !attw) {
+        free(loc);
+        free(attw);
+        return 3;
+    }
+    for (int64_t r = 0; r < rows; ++r) {
+        const int64_t nq = r / M;  /* row r = (n*Lq + q)*M + m */
+        const double* z = attention_logits + r * LP;
+        double zmax = z[0];
+        for (int64_t s = 1; s < LP; ++s)
+            if (z[s] > zmax) zmax = z[s];
+        double denom = 0.0;
+        for (int64_t s = 0; s < LP; ++s) denom += exp(z[s] - zmax);
+        for (int64_t s = 0; s < LP; ++s) {
+            attw[r * LP + s] = exp(z[s] - zmax) / denom;
+            for (int c = 0; c < dims; ++c) {
+                const float ref = reference_points[nq * dims + c];
+                const float off = sampling_offsets[(r * LP + s) * dims + c];
+                loc[(r * LP + s) * dims + c] = ref + off;
+            }
+        }
+    }
+    const int rc = dims == 2
+        ? msda_oracle_forward(value, spatial_shapes, level_start_index, loc, attw, out,
+                              N, S, M, D, Lq, L, P)
+        : msda3d_oracle_forward(value, spatial_shapes, level_start_index, loc, attw, out,
+                                N, S, M, D, Lq, L, P);
+    free(loc);
+    free(attw);
+    return rc;
+}
+
+int msda_oracle_forward_fused(const double* value, const int64_t* spatial_shapes,
+                              const int64_t* level_start_index,
+                              const float* reference_points, const float* sampling_offsets,
+                              const double* attention_logits, double* out,
+                              int64_t N, int64_t S, int64_t M, int64_t D,
+                              int64_t Lq, int64_t L, int64_t P) {
+    return forward_fused(2, value, spatial_shapes, level_start_index, reference_points,
+                         sampling_offsets, attention_logits, out, N, S, M, D, Lq, L, P);
+}
+
+int msda3d_oracle_forward_fused(const double* value, const int64_t* spatial_shapes,
+                                const int64_t* level_start_index,
+                                const float* reference_points, const float* sampling_offsets,
+                                const double* attention_logits, double* out,
+                                int64_t N, int64_t S, int64_t M, int64_t D,
+                                int64_t Lq, int64_t L, int64_t P) {
+    return forward_fused(3, value, spatial_shapes, level_start_index, reference_points,
+                         sampling_offsets, attention_logits, out, N, S, M, D, Lq, L, P);
 }

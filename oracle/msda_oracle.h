@@ -106,6 +106,31 @@ int msda3d_oracle_backward(const double* value, const int64_t* spatial_shapes,
                            int64_t N, int64_t S, int64_t M, int64_t D,
                            int64_t Lq, int64_t L, int64_t P);
 
+/*
+ * Forward with the module's front end: attention weights are the softmax over
+ * the L*P samples of each (n, q, m) of attention_logits (double, widened from
+ * fp32), computed in fp64; sampling location = reference_points[n][q] +
+ * sampling_offsets[n][q][m][l][p], one fp32 addition per coordinate.  Then
+ * exactly msda_oracle_forward / msda3d_oracle_forward.
+ *   reference_points  float  [N][Lq][dims]
+ *   sampling_offsets  float  [N][Lq][M][L][P][dims]
+ *   attention_logits  double [N][Lq][M][L][P]
+ * Returns 3 if the temporaries cannot be allocated; otherwise as the core.
+ */
+int msda_oracle_forward_fused(const double* value, const int64_t* spatial_shapes,
+                              const int64_t* level_start_index,
+                              const float* reference_points, const float* sampling_offsets,
+                              const double* attention_logits, double* out,
+                              int64_t N, int64_t S, int64_t M, int64_t D,
+                              int64_t Lq, int64_t L, int64_t P);
+
+int msda3d_oracle_forward_fused(const double* value, const int64_t* spatial_shapes,
+                                const int64_t* level_start_index,
+                                const float* reference_points, const float* sampling_offsets,
+                                const double* attention_logits, double* out,
+                                int64_t N, int64_t S, int64_t M, int64_t D,
+                                int64_t Lq, int64_t L, int64_t P);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,7 +1,8 @@
 """Python binding of the C ABI in ``include/msda.h`` (argument marshalling only).
 
-``msda_forward`` / ``msda3d_forward`` and ``msda_backward`` /
-``msda3d_backward`` take torch tensors that already live on the GPU, check
+``msda_forward`` / ``msda3d_forward``, ``msda_forward_fused`` /
+``msda3d_forward_fused`` and ``msda_backward`` / ``msda3d_backward`` take
+torch tensors that already live on the GPU, check
 dtypes/shapes/contiguity, allocate outputs with torch when the caller passes
 none, and call the same-named C entry point of ``libmsda.so`` on torch's
 current HIP stream.  Every step of the computation
@@ -33,8 +34,8 @@ STATUS = {
 }
 
 # Every symbol include/msda.h declares.
-EXPORTED = ("msda_forward", "msda3d_forward", "msda_backward", "msda3d_backward",
-            "msda_status_string")
+EXPORTED = ("msda_forward", "msda3d_forward", "msda_forward_fused", "msda3d_forward_fused",
+            "msda_backward", "msda3d_backward", "msda_status_string")
 
 _lib = None
 
@@ -68,6 +69,11 @@ def load_library() -> ctypes.CDLL:
         fn.restype = ctypes.c_int
         fn.argtypes = [vp, ctypes.c_int, vp, vp, vp, vp, vp, ctypes.c_int,
                        i64, i64, i64, i64, i64, i64, i64, vp]
+    for name in ("msda_forward_fused", "msda3d_forward_fused"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [vp, ctypes.c_int, vp, vp, vp, vp, vp, vp, ctypes.c_int,
+                       i64, i64, i64, i64, i64, i64, i64, vp]
     for name in ("msda_backward", "msda3d_backward"):
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
@@ -91,6 +97,17 @@ def raw_call(dims: int, value_ptr: int, value_dtype: int, shapes_ptr: int,
     lib = load_library()
     fn = lib.msda_forward if dims == 2 else lib.msda3d_forward
     return fn(value_ptr, value_dtype, shapes_ptr, starts_ptr, loc_ptr, attw_ptr,
+              out_ptr, out_dtype, N, S, M, D, Lq, L, P, stream)
+
+
+def raw_fused_call(dims: int, value_ptr: int, value_dtype: int, shapes_ptr: int,
+                   starts_ptr: int, ref_ptr: int, off_ptr: int, logits_ptr: int, out_ptr: int,
+                   out_dtype: int, N: int, S: int, M: int, D: int, Lq: int, L: int, P: int,
+                   stream: int = 0) -> int:
+    """Call the fused-front-end forward with raw pointers; returns the msda_status."""
+    lib = load_library()
+    fn = lib.msda_forward_fused if dims == 2 else lib.msda3d_forward_fused
+    return fn(value_ptr, value_dtype, shapes_ptr, starts_ptr, ref_ptr, off_ptr, logits_ptr,
               out_ptr, out_dtype, N, S, M, D, Lq, L, P, stream)
 
 
@@ -244,3 +261,48 @@ def msda3d_backward(value, spatial_shapes, level_start_index, sampling_locations
     return _backward(3, value, spatial_shapes, level_start_index, sampling_locations,
                      attention_weights, grad_out, grad_value, grad_sampling_locations,
                      grad_attention_weights, stream)
+
+
+def _forward_fused(dims, value, spatial_shapes, level_start_index, reference_points,
+                   sampling_offsets, attention_logits, out, out_dtype, stream):
+    code, N, S, M, D, Lq, L, P = _check_inputs(dims, value, spatial_shapes, level_start_index,
+                                               sampling_offsets, attention_logits)
+    if (not reference_points.is_cuda or not reference_points.is_contiguous()
+            or reference_points.dtype != torch.float32
+            or tuple(reference_points.shape) != (N, Lq, dims)):
+        raise ValueError(f"reference_points must be a contiguous float32 [N, Lq, {dims}] "
+                         "GPU tensor")
+    if out is None:
+        dt = value.dtype if out_dtype is None else out_dtype
+        out = torch.empty((N, Lq, M * D), dtype=dt, device=value.device)
+    elif (out.shape != (N, Lq, M * D) or not out.is_contiguous()
+          or out.device != value.device or (out_dtype is not None and out.dtype != out_dtype)):
+        raise ValueError("out must be a contiguous [N, Lq, M*D] tensor on value's device")
+    out_code = _dtype_code(out.dtype, "out")
+    s = stream if stream is not None else torch.cuda.current_stream(value.device)
+    status = raw_fused_call(dims, value.data_ptr(), code, spatial_shapes.data_ptr(),
+                            level_start_index.data_ptr(), reference_points.data_ptr(),
+                            sampling_offsets.data_ptr(), attention_logits.data_ptr(),
+                            out.data_ptr(), out_code, N, S, M, D, Lq, L, P, s.cuda_stream)
+    if status != 0:
+        raise MsdaError(status, status_string(status))
+    return out
+
+
+def msda_forward_fused(value, spatial_shapes, level_start_index, reference_points,
+                       sampling_offsets, attention_logits, out=None, out_dtype=None,
+                       stream=None) -> torch.Tensor:
+    """2D MSDA forward with the front end fused: attention weights = softmax of
+    ``attention_logits`` [N,Lq,M,L,P] over the L*P samples of each (n, q, m),
+    locations = ``reference_points`` [N,Lq,2] + ``sampling_offsets``
+    [N,Lq,M,L,P,2] (fp32); otherwise as ``msda_forward``."""
+    return _forward_fused(2, value, spatial_shapes, level_start_index, reference_points,
+                          sampling_offsets, attention_logits, out, out_dtype, stream)
+
+
+def msda3d_forward_fused(value, spatial_shapes, level_start_index, reference_points,
+                         sampling_offsets, attention_logits, out=None, out_dtype=None,
+                         stream=None) -> torch.Tensor:
+    """3D counterpart of ``msda_forward_fused`` (3-component points)."""
+    return _forward_fused(3, value, spatial_shapes, level_start_index, reference_points,
+                          sampling_offsets, attention_logits, out, out_dtype, stream)

@@ -1,5 +1,6 @@
-// C ABI of the MSDA forward core (declared in include/msda.h): argument
-// validation, launch-shape selection and the kernel dispatch.
+// C ABI of the MSDA core (declared in include/msda.h): argument validation,
+// launch-shape selection and the kernel dispatch of the forward, the forward
+// with the fused front end, and the backward.
 //
 // Nothing here allocates, frees or synchronises; every argument check runs on
 // the host before the first HIP call.
@@ -52,32 +53,32 @@ int ceil_log2(int64_t x) {
     return r;
 }
 
-template <typename TV, typename TO, int DIM, int CPL>
+template <typename TV, typename TO, int DIM, int CPL, bool FUSED>
 void launch_one(const Params& p, hipStream_t stream) {
-    hipLaunchKernelGGL((msda::msda_forward_kernel<TV, TO, DIM, CPL>), dim3(p.num_blocks),
+    hipLaunchKernelGGL((msda::msda_forward_kernel<TV, TO, DIM, CPL, FUSED>), dim3(p.num_blocks),
                        dim3(msda::kBlockThreads), 0, stream, p);
 }
 
-template <typename TV, typename TO, int DIM, int CPL>
+template <typename TV, typename TO, int DIM, int CPL, bool FUSED>
 void launch_staged_one(const StagedParams& sp, hipStream_t stream) {
     static_assert(MSDA_STAGE_BUDGET <= 64 * 1024, "dynamic LDS above the default limit");
     if constexpr (DIM == 2)  // the staged kernel is only launched for 2D pyramids
-        hipLaunchKernelGGL((msda::msda_forward_staged_kernel<TV, TO, DIM, CPL>),
+        hipLaunchKernelGGL((msda::msda_forward_staged_kernel<TV, TO, DIM, CPL, FUSED>),
                            dim3(sp.p.num_blocks), dim3(msda::kStagedThreads), sp.stage_bytes,
                            stream, sp);
 }
 
 // Kernel selection by CPL (lanes per head row), then by value/out type.
-template <typename TV, typename TO, int DIM, typename P>
+template <typename TV, typename TO, int DIM, bool FUSED, typename P>
 void launch_cpl(int cpl, const P& p, hipStream_t stream) {
     constexpr bool staged = std::is_same<P, StagedParams>::value;
     switch (cpl) {
-#define MSDA_CASE(C)                                          \
-    case C:                                                   \
-        if constexpr (staged)                                 \
-            launch_staged_one<TV, TO, DIM, C>(p, stream);     \
-        else                                                  \
-            launch_one<TV, TO, DIM, C>(p, stream);            \
+#define MSDA_CASE(C)                                             \
+    case C:                                                      \
+        if constexpr (staged)                                    \
+            launch_staged_one<TV, TO, DIM, C, FUSED>(p, stream); \
+        else                                                     \
+            launch_one<TV, TO, DIM, C, FUSED>(p, stream);        \
         break;
         MSDA_CASE(1)
         MSDA_CASE(2)
@@ -87,26 +88,26 @@ void launch_cpl(int cpl, const P& p, hipStream_t stream) {
         MSDA_CASE(32)
         default:
             if constexpr (staged)
-                launch_staged_one<TV, TO, DIM, 64>(p, stream);
+                launch_staged_one<TV, TO, DIM, 64, FUSED>(p, stream);
             else
-                launch_one<TV, TO, DIM, 64>(p, stream);
+                launch_one<TV, TO, DIM, 64, FUSED>(p, stream);
             break;
 #undef MSDA_CASE
     }
 }
 
-template <int DIM, typename P>
+template <int DIM, bool FUSED, typename P>
 void launch(int value_dtype, int out_dtype, int cpl, const P& p, hipStream_t stream) {
     if (value_dtype == MSDA_F32) {
         if (out_dtype == MSDA_F32)
-            launch_cpl<float, float, DIM>(cpl, p, stream);
+            launch_cpl<float, float, DIM, FUSED>(cpl, p, stream);
         else
-            launch_cpl<float, msda::Bf16, DIM>(cpl, p, stream);
+            launch_cpl<float, msda::Bf16, DIM, FUSED>(cpl, p, stream);
     } else {
         if (out_dtype == MSDA_F32)
-            launch_cpl<msda::Bf16, float, DIM>(cpl, p, stream);
+            launch_cpl<msda::Bf16, float, DIM, FUSED>(cpl, p, stream);
         else
-            launch_cpl<msda::Bf16, msda::Bf16, DIM>(cpl, p, stream);
+            launch_cpl<msda::Bf16, msda::Bf16, DIM, FUSED>(cpl, p, stream);
     }
 }
 
@@ -116,18 +117,20 @@ bool aligned(const void* ptr, uintptr_t a) {
     return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) == 0;
 }
 
-template <int DIM>
+// FUSED: sampling_locations holds the offsets, attention_weights the logits,
+// and reference_points [N][Lq][DIM] the reference points.
+template <int DIM, bool FUSED>
 int forward(const void* value, int value_dtype, const int64_t* spatial_shapes,
             const int64_t* level_start_index, const float* sampling_locations,
             const float* attention_weights, void* out, int out_dtype, int64_t N,
             int64_t S, int64_t M, int64_t D, int64_t Lq, int64_t L, int64_t P,
-            void* stream) {
+            void* stream, const float* reference_points = nullptr) {
     if (N < 0 || Lq < 0 || S < 1 || M < 1 || D < 1 || L < 1 || P < 1)
         return MSDA_ERR_DIM;
     if (!known_dtype(value_dtype) || !known_dtype(out_dtype)) return MSDA_ERR_DTYPE;
     if (N == 0 || Lq == 0) return MSDA_OK;
     if (!value || !spatial_shapes || !level_start_index || !sampling_locations ||
-        !attention_weights || !out)
+        !attention_weights || !out || (FUSED && !reference_points))
         return MSDA_ERR_NULL;
 
     const int64_t elem = value_dtype == MSDA_F32 ? 4 : 2;
@@ -139,7 +142,7 @@ int forward(const void* value, int value_dtype, const int64_t* spatial_shapes,
 
     if (!aligned(value, 16) || !aligned(out, 16) || !aligned(sampling_locations, 4) ||
         !aligned(attention_weights, 4) || !aligned(spatial_shapes, 8) ||
-        !aligned(level_start_index, 8))
+        !aligned(level_start_index, 8) || (FUSED && !aligned(reference_points, 4)))
         return MSDA_ERR_ALIGN;
 
     // One image's value must be addressable with 32-bit byte offsets.
@@ -220,6 +223,10 @@ int forward(const void* value, int value_dtype, const int64_t* spatial_shapes,
             p.div_wps = make_fast_div(static_cast<uint32_t>(waves_per_slice));
             p.div_M = make_fast_div(static_cast<uint32_t>(M));
             p.div_P = make_fast_div(static_cast<uint32_t>(P));
+            if (FUSED) {
+                p.ref = reference_points + (n0 * Lq + q0) * DIM;
+                p.ref_bytes = static_cast<uint32_t>(nbatch * nquery * DIM * 4);
+            }
 
             // Staged kernel: large 2D launches whose phase-B iterations are
             // level-pure (G divides P), with MSDA_STAGED_WGS_PER_SLICE
@@ -244,12 +251,12 @@ int forward(const void* value, int value_dtype, const int64_t* spatial_shapes,
                 sp.div_wgs = make_fast_div(static_cast<uint32_t>(wgs_per_slice));
                 sp.stage_bytes = static_cast<uint32_t>(stage);
                 sp.ipl = static_cast<int32_t>(P / G);
-                launch<DIM>(value_dtype, out_dtype, cpl, sp, hs);
+                launch<DIM, FUSED>(value_dtype, out_dtype, cpl, sp, hs);
                 if (hipGetLastError() != hipSuccess) return MSDA_ERR_LAUNCH;
                 continue;
             }
 
-            launch<DIM>(value_dtype, out_dtype, cpl, p, hs);
+            launch<DIM, FUSED>(value_dtype, out_dtype, cpl, p, hs);
             if (hipGetLastError() != hipSuccess) return MSDA_ERR_LAUNCH;
         }
     }
@@ -435,9 +442,9 @@ int msda_forward(const void* value, int value_dtype, const int64_t* spatial_shap
                  const float* attention_weights, void* out, int out_dtype, int64_t N,
                  int64_t S, int64_t M, int64_t D, int64_t Lq, int64_t L, int64_t P,
                  void* stream) {
-    return forward<2>(value, value_dtype, spatial_shapes, level_start_index,
-                      sampling_locations, attention_weights, out, out_dtype, N, S, M, D, Lq,
-                      L, P, stream);
+    return forward<2, false>(value, value_dtype, spatial_shapes, level_start_index,
+                             sampling_locations, attention_weights, out, out_dtype, N, S, M, D,
+                             Lq, L, P, stream);
 }
 
 int msda3d_forward(const void* value, int value_dtype, const int64_t* spatial_shapes,
@@ -445,9 +452,29 @@ int msda3d_forward(const void* value, int value_dtype, const int64_t* spatial_sh
                    const float* attention_weights, void* out, int out_dtype, int64_t N,
                    int64_t S, int64_t M, int64_t D, int64_t Lq, int64_t L, int64_t P,
                    void* stream) {
-    return forward<3>(value, value_dtype, spatial_shapes, level_start_index,
-                      sampling_locations, attention_weights, out, out_dtype, N, S, M, D, Lq,
-                      L, P, stream);
+    return forward<3, false>(value, value_dtype, spatial_shapes, level_start_index,
+                             sampling_locations, attention_weights, out, out_dtype, N, S, M, D,
+                             Lq, L, P, stream);
+}
+
+int msda_forward_fused(const void* value, int value_dtype, const int64_t* spatial_shapes,
+                       const int64_t* level_start_index, const float* reference_points,
+                       const float* sampling_offsets, const float* attention_logits, void* out,
+                       int out_dtype, int64_t N, int64_t S, int64_t M, int64_t D, int64_t Lq,
+                       int64_t L, int64_t P, void* stream) {
+    return forward<2, true>(value, value_dtype, spatial_shapes, level_start_index,
+                            sampling_offsets, attention_logits, out, out_dtype, N, S, M, D, Lq,
+                            L, P, stream, reference_points);
+}
+
+int msda3d_forward_fused(const void* value, int value_dtype, const int64_t* spatial_shapes,
+                         const int64_t* level_start_index, const float* reference_points,
+                         const float* sampling_offsets, const float* attention_logits,
+                         void* out, int out_dtype, int64_t N, int64_t S, int64_t M, int64_t D,
+                         int64_t Lq, int64_t L, int64_t P, void* stream) {
+    return forward<3, true>(value, value_dtype, spatial_shapes, level_start_index,
+                            sampling_offsets, attention_logits, out, out_dtype, N, S, M, D, Lq,
+                            L, P, stream, reference_points);
 }
 
 int msda_backward(const void* value, int value_dtype, const int64_t* spatial_shapes,

@@ -320,7 +320,7 @@ __global__ __launch_bounds__(kBlockThreads) void msda_backward_kernel(BwdParams 
 
 // grad_value = 0 before the scatter (a plain fill kernel: no memset node in
 // a captured graph).
-__global__ __launch_bounds__(256) void msda_zero_kernel(float4* p, uint64_t n4) {
+static __global__ __launch_bounds__(256) void msda_zero_kernel(float4* p, uint64_t n4) {
     const uint64_t stride = static_cast<uint64_t>(gridDim.x) * blockDim.x;
     for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n4; i += stride)
         p[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);

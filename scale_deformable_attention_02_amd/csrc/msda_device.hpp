@@ -106,6 +106,10 @@ struct Params {
     FastDiv div_wps;              // wave -> slice n*M + m
     FastDiv div_M;                // slice -> n
     FastDiv div_P;                // sample -> level
+    // fused front end only: loc holds the offsets, attw the logits, and ref
+    // the reference points, at (n0, q0): rows (n*Lq + q) of DIM floats
+    const float* ref;
+    uint32_t ref_bytes;
 };
 
 // One sample's contribution recipe: NC corner byte offsets (relative to the
@@ -322,6 +326,54 @@ __device__ __forceinline__ void load_sample(const Params& p, bool live, uint32_t
         __builtin_amdgcn_raw_buffer_load_b32(rattw, attw_off, 0, MSDA_STREAM_AUX));
 }
 
+// Fused front end, load step: the offset (into xyz), the logit (into a) and
+// the reference point of query row qrow (n*Lq + q of this launch).  Dead lanes
+// get a logit of -inf.
+template <int DIM>
+__device__ __forceinline__ void load_sample_fused(const Params& p, bool live, uint32_t sidx,
+                                                  uint32_t qrow, float (&xyz)[DIM], float& a,
+                                                  float (&ref)[DIM]) {
+    load_sample<DIM>(p, live, sidx, xyz, a);
+    const __amdgpu_buffer_rsrc_t rref = buffer_of(p.ref, p.ref_bytes);
+    const uint32_t ref_off = live ? qrow * (DIM * 4u) : kOutOfRange;
+    if constexpr (DIM == 2) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(rref, ref_off, 0, MSDA_STREAM_AUX);
+        ref[0] = __uint_as_float(v[0]);
+        ref[1] = __uint_as_float(v[1]);
+    } else {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b96(rref, ref_off, 0, MSDA_STREAM_AUX);
+        ref[0] = __uint_as_float(v[0]);
+        ref[1] = __uint_as_float(v[1]);
+        ref[2] = __uint_as_float(v[2]);
+    }
+    if (!live) a = -__builtin_inff();
+}
+
+// Fused front end, finish step: location = reference point + offset (one fp32
+// add per coordinate), and the attention weight = softmax of the logits over
+// the tile's L*P samples.  The lanes of one tile differ only in the bits below
+// log2G (point group within the tile) and from log2NG up (iteration), so a
+// butterfly over those bits reduces exactly over the tile.
+template <int DIM, int LOG2NG>
+__device__ __forceinline__ void finish_sample_fused(bool live, int log2G, float (&xyz)[DIM],
+                                                    float& a, const float (&ref)[DIM]) {
+#pragma unroll
+    for (int d = 0; d < DIM; ++d) xyz[d] = ref[d] + xyz[d];
+    float mx = a;
+    for (int b = 0; b < log2G; ++b) mx = fmaxf(mx, __shfl_xor(mx, 1 << b, kWave));
+#pragma unroll
+    for (int b = LOG2NG; b < 6; ++b) mx = fmaxf(mx, __shfl_xor(mx, 1 << b, kWave));
+    const float e = live ? expf(a - mx) : 0.0f;
+    float sum = e;
+    for (int b = 0; b < log2G; ++b) sum += __shfl_xor(sum, 1 << b, kWave);
+#pragma unroll
+    for (int b = LOG2NG; b < 6; ++b) sum += __shfl_xor(sum, 1 << b, kWave);
+    a = live ? e / sum : 0.0f;
+}
+
+template <int N>
+constexpr int ilog2() { return N <= 1 ? 0 : 1 + ilog2<N / 2>(); }
+
 template <typename TV, int NC, int VEC>
 __device__ __forceinline__ void fma_corners(const Slot<NC>& sl, const uint32_t (&raw)[NC][4],
                                             float (&acc)[VEC]) {
@@ -405,7 +457,7 @@ __device__ __forceinline__ void wave_lds_sync() {
 // Direct kernel: one pass of T tiles per wave, every corner gathered from HBM
 // (through L2/L1).  Used for small problems and as the general path.
 // ---------------------------------------------------------------------------
-template <typename TV, typename TO, int DIM, int CPL>
+template <typename TV, typename TO, int DIM, int CPL, bool FUSED = false>
 __global__ __launch_bounds__(kBlockThreads) void msda_forward_kernel(Params p) {
     constexpr int NC = DIM == 2 ? 4 : 8;     // corners per sample
     constexpr int NG = kWave / CPL;          // point groups per wave
@@ -449,7 +501,14 @@ __global__ __launch_bounds__(kBlockThreads) void msda_forward_kernel(Params p) {
                               static_cast<uint32_t>(t) * static_cast<uint32_t>(p.M * p.LP) +
                               static_cast<uint32_t>(s_c);
         float xyz[DIM], a;
-        load_sample<DIM>(p, live, sidx, xyz, a);
+        if constexpr (FUSED) {
+            float ref[DIM];
+            const uint32_t qrow = n * static_cast<uint32_t>(p.Lq) + q0 + static_cast<uint32_t>(t);
+            load_sample_fused<DIM>(p, live, sidx, qrow, xyz, a, ref);
+            finish_sample_fused<DIM, ilog2<NG>()>(live, p.log2G, xyz, a, ref);
+        } else {
+            load_sample<DIM>(p, live, sidx, xyz, a);
+        }
 
         __syncthreads();  // smeta is ready
         const LevelGeom lg = smeta[s_c];
@@ -501,7 +560,7 @@ struct StagedParams {
     int32_t ipl;             // phase-B iterations per level, P / G
 };
 
-template <typename TV, typename TO, int DIM, int CPL>
+template <typename TV, typename TO, int DIM, int CPL, bool FUSED = false>
 __global__ __launch_bounds__(kStagedThreads) void msda_forward_staged_kernel(StagedParams sp) {
     constexpr int NC = DIM == 2 ? 4 : 8;
     constexpr int NG = kWave / CPL;
@@ -625,26 +684,28 @@ __global__ __launch_bounds__(kStagedThreads) void msda_forward_staged_kernel(Sta
     // Locations and weights of the first chunk; each later chunk's are loaded
     // one chunk ahead.
     uint32_t q0 = qa + static_cast<uint32_t>(wave * p.T);
-    float xyz[DIM], a;
+    float xyz[DIM], a, ref[DIM];
+    const auto load = [&](uint32_t q, bool lv) {
+        const uint32_t qrow = n * static_cast<uint32_t>(p.Lq) + q;
+        const uint32_t sidx = (qrow * static_cast<uint32_t>(p.M) + m) * lp + lane_rel;
+        if constexpr (FUSED)
+            load_sample_fused<DIM>(p, lv, sidx, qrow + static_cast<uint32_t>(ta), xyz, a, ref);
+        else
+            load_sample<DIM>(p, lv, sidx, xyz, a);
+    };
     bool live = lane_has_sample && q0 + static_cast<uint32_t>(ta) < qb;
-    load_sample<DIM>(p, live,
-                     ((n * static_cast<uint32_t>(p.Lq) + q0) * static_cast<uint32_t>(p.M) + m) * lp +
-                         lane_rel,
-                     xyz, a);
+    load(q0, live);
     for (uint32_t qc = qa; qc < qb; qc += stride) {
         const uint32_t row0 = (n * static_cast<uint32_t>(p.Lq) + q0) * static_cast<uint32_t>(p.M) + m;
 
         // ---- Phase A
+        if constexpr (FUSED) finish_sample_fused<DIM, ilog2<NG>()>(live, p.log2G, xyz, a, ref);
         slots[wave][lane] = make_slot<DIM>(xyz, a, live, lga, slot_base, slot_stride, slot_invalid);
         const uint32_t q_this = q0;
         q0 += stride;
         if (qc + stride < qb) {
             live = lane_has_sample && q0 + static_cast<uint32_t>(ta) < qb;
-            load_sample<DIM>(
-                p, live,
-                ((n * static_cast<uint32_t>(p.Lq) + q0) * static_cast<uint32_t>(p.M) + m) * lp +
-                    lane_rel,
-                xyz, a);
+            load(q0, live);
         }
         wave_lds_sync();
 

@@ -21,8 +21,10 @@ order):
      added to the reference point (float32);
   4. logits ~ N(0, 1) per (n, q, m, l, p); attention weights are their softmax
      over the L*P samples of each (n, q, m), taken in float64, stored float32.
-For a backward pass ``make_grad_out`` draws the output gradient ~ N(0, 1)
-from a generator of its own.
+``make_fused_inputs`` returns the draws of steps 2-4 before they are
+combined (reference points, offsets, logits), for the forward with the fused
+front end.  For a backward pass ``make_grad_out`` draws the output gradient
+~ N(0, 1) from a generator of its own.
 """
 from __future__ import annotations
 
@@ -158,14 +160,10 @@ def pixel_centre_refs(shapes, dims: int) -> torch.Tensor:
     return torch.cat(refs, dim=0)
 
 
-def make_inputs(w: Workload, seed: Optional[int] = None) -> Dict[str, torch.Tensor]:
-    """Draw one batch of inputs for workload ``w`` on the CPU.
-
-    Returns a dict with ``value`` ([N,S,M,D], float32 or bfloat16),
-    ``spatial_shapes`` (int64 [L, dims]), ``level_start_index`` (int64 [L]),
-    ``sampling_locations`` (float32 [N,Lq,M,L,P,dims]) and
-    ``attention_weights`` (float32 [N,Lq,M,L,P]).
-    """
+def _draw(w: Workload, seed: Optional[int]):
+    """The seeded draws of the recipe, in order: value, reference points (None
+    for ``uniform`` workloads, whose locations are drawn directly), offsets or
+    locations, logits."""
     g = torch.Generator(device="cpu")
     g.manual_seed(w.seed if seed is None else seed)
     N, S, M, D, L, P, dims = w.N, w.S, w.M, w.D, w.L, w.P, w.dims
@@ -178,11 +176,12 @@ def make_inputs(w: Workload, seed: Optional[int] = None) -> Dict[str, torch.Tens
         raise ValueError(f"unknown value dtype {w.value_dtype!r}")
 
     loc_shape = (N, Lq, M, L, P, dims)
+    ref = None
     if w.queries == "uniform":
         lo, hi = w.box
-        loc = torch.rand(loc_shape, generator=g, dtype=torch.float32) * (hi - lo) + lo
+        off = torch.rand(loc_shape, generator=g, dtype=torch.float32) * (hi - lo) + lo
         if w.sigma:
-            loc = loc + torch.randn(loc_shape, generator=g, dtype=torch.float32) * w.sigma
+            off = off + torch.randn(loc_shape, generator=g, dtype=torch.float32) * w.sigma
     else:
         if w.queries == "random_refs":
             ref = torch.rand((N, Lq, dims), generator=g, dtype=torch.float32)
@@ -190,25 +189,60 @@ def make_inputs(w: Workload, seed: Optional[int] = None) -> Dict[str, torch.Tens
             if Lq != S:
                 raise ValueError("pixel-centre queries need Lq == S")
             ref = pixel_centre_refs(w.shapes, dims).to(torch.float32)
-            ref = ref.unsqueeze(0).expand(N, S, dims)
+            ref = ref.unsqueeze(0).expand(N, S, dims).contiguous()
         else:
             raise ValueError(f"unknown query layout {w.queries!r}")
         off = torch.randn(loc_shape, generator=g, dtype=torch.float32) * w.sigma
-        loc = ref.reshape(N, Lq, 1, 1, 1, dims) + off
-    loc = loc.contiguous()
 
     logits = torch.randn((N, Lq, M, L * P), generator=g, dtype=torch.float32)
-    attw = torch.softmax(logits.to(torch.float64), dim=-1).to(torch.float32)
-    attw = attw.reshape(N, Lq, M, L, P).contiguous()
-
     shapes = torch.tensor(w.shapes, dtype=torch.int64).reshape(L, dims)
     starts = torch.tensor(level_starts(w.shapes), dtype=torch.int64)
+    return value.contiguous(), shapes, starts, ref, off.contiguous(), logits
+
+
+def make_inputs(w: Workload, seed: Optional[int] = None) -> Dict[str, torch.Tensor]:
+    """Draw one batch of inputs for workload ``w`` on the CPU.
+
+    Returns a dict with ``value`` ([N,S,M,D], float32 or bfloat16),
+    ``spatial_shapes`` (int64 [L, dims]), ``level_start_index`` (int64 [L]),
+    ``sampling_locations`` (float32 [N,Lq,M,L,P,dims]) and
+    ``attention_weights`` (float32 [N,Lq,M,L,P]).
+    """
+    value, shapes, starts, ref, off, logits = _draw(w, seed)
+    N, Lq, M, L, P, dims = off.shape
+    if ref is None:
+        loc = off
+    else:
+        loc = (ref.reshape(N, Lq, 1, 1, 1, dims) + off).contiguous()
+    attw = torch.softmax(logits.to(torch.float64), dim=-1).to(torch.float32)
+    attw = attw.reshape(N, Lq, M, L, P).contiguous()
     return {
-        "value": value.contiguous(),
+        "value": value,
         "spatial_shapes": shapes,
         "level_start_index": starts,
         "sampling_locations": loc,
         "attention_weights": attw,
+    }
+
+
+def make_fused_inputs(w: Workload, seed: Optional[int] = None) -> Dict[str, torch.Tensor]:
+    """The same draws as ``make_inputs`` before the front end: ``reference_points``
+    (float32 [N,Lq,dims]; zeros for ``uniform`` workloads, whose offsets are
+    then the drawn locations), ``sampling_offsets`` (float32 [N,Lq,M,L,P,dims])
+    and ``attention_logits`` (float32 [N,Lq,M,L,P]), plus value, shapes and
+    level starts.  reference + offset in fp32 equals make_inputs' locations
+    bit for bit."""
+    value, shapes, starts, ref, off, logits = _draw(w, seed)
+    N, Lq, M, L, P, dims = off.shape
+    if ref is None:
+        ref = torch.zeros((N, Lq, dims), dtype=torch.float32)
+    return {
+        "value": value,
+        "spatial_shapes": shapes,
+        "level_start_index": starts,
+        "reference_points": ref.contiguous(),
+        "sampling_offsets": off,
+        "attention_logits": logits.reshape(N, Lq, M, L, P).contiguous(),
     }
 
 

@@ -45,6 +45,16 @@ def test_library_exports_every_declared_symbol(lib):
         assert name in exported, name
 
 
+def test_argtypes_match_the_header(lib):
+    # every bound entry point passes as many arguments as the header declares
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    for name in binding.EXPORTED:
+        m = re.search(r"\b" + name + r"\s*\(([^)]*)\)", text)
+        assert m, name
+        declared = len([a for a in m.group(1).split(",") if a.strip()])
+        assert len(getattr(lib, name).argtypes) == declared, name
+
+
 def test_status_strings(lib):
     for code in range(8):
         s = binding.status_string(code)
@@ -163,3 +173,27 @@ def test_backward_unsupported_misaligned_overflow(lib):
     # fp32 gradient image S*M*D*4 must stay below 2^31 bytes, also for bf16 value
     assert bcall(S=(1 << 31) // (8 * 32 * 4), M=8, D=32, dtype=1) == OVERFLOW
     assert bcall(M=1 << 31, D=4) == OVERFLOW
+
+
+# ---- fused front end: the forward's checks plus the reference-point pointer
+
+def fcall(dims=2, ref=A, **kw):
+    args = dict(value=A, dtype=0, shapes=A, starts=A, loc=A, attw=A, out=A, out_dtype=0,
+                N=1, S=100, M=8, D=32, Lq=10, L=4, P=4)
+    args.update(kw)
+    return binding.raw_fused_call(dims, args["value"], args["dtype"], args["shapes"],
+                                  args["starts"], ref, args["loc"], args["attw"], args["out"],
+                                  args["out_dtype"], args["N"], args["S"], args["M"], args["D"],
+                                  args["Lq"], args["L"], args["P"], 0)
+
+
+@pytest.mark.parametrize("dims", [2, 3])
+def test_fused_checks(lib, dims):
+    assert fcall(dims, ref=0) == NULL
+    assert fcall(dims, ref=A + 2) == ALIGN
+    for k in ("value", "shapes", "starts", "loc", "attw", "out"):
+        assert fcall(dims, **{k: 0}) == NULL, k
+    assert fcall(dims, D=3) == UNSUP
+    assert fcall(dims, dtype=5) == DTYPE
+    assert fcall(dims, S=1 << 31, M=1, D=4) == OVERFLOW
+    assert fcall(dims, N=0, ref=0, value=0, out=0, loc=0, attw=0) == OK
