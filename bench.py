@@ -8,7 +8,10 @@ M=8, D=32, L=4, P=4, fp32), inputs already resident in HBM.  With
 plus the gradient kernel) on the same inputs and an N(0,1) output gradient;
 with ``--op forward_fused`` one msda_forward_fused call on the same draws
 before the front end (reference points, offsets, logits), and the unfused
-pipeline (torch softmax + add, then msda_forward) is timed beside it.
+pipeline (torch softmax + add, then msda_forward) is timed beside it; with
+``--op forward_pruned`` one msda_forward_pruned call at ``--prune-threshold``
+(the fraction of samples it drops and the unpruned kernel's time on the same
+inputs are reported beside it).
 Steps cycle over several distinct copies of the inputs whose total exceeds
 twice the 256 MB Infinity Cache, so each step reads its inputs from HBM
 rather than from a cache warmed by the previous step.
@@ -36,6 +39,8 @@ if ROOT not in sys.path:
 METRIC = "sampled points/sec + achieved HBM GB/s (DETR encoder shape, 1 MI355X)"
 METRIC_BACKWARD = ("backward sampled points/sec + achieved HBM GB/s "
                    "(DETR encoder shape, 1 MI355X)")
+METRIC_PRUNED = ("pruned forward sampled points/sec + achieved HBM GB/s "
+                 "(DETR encoder shape, 1 MI355X)")
 METRIC_FUSED = ("fused front end + forward sampled points/sec + achieved HBM GB/s "
                 "(DETR encoder shape, 1 MI355X)")
 HBM_PEAK_GBPS = 8000.0
@@ -44,11 +49,13 @@ CSRC = os.path.join(ROOT, "scale_deformable_attention_02_amd", "csrc")
 COUNTERS_FILES = {
     "forward": os.path.join(ROOT, "profiles", "msda_forward_counters.json"),
     "forward_fused": os.path.join(ROOT, "profiles", "msda_forward_fused_counters.json"),
+    "forward_pruned": os.path.join(ROOT, "profiles", "msda_forward_pruned_counters.json"),
     "backward": os.path.join(ROOT, "profiles", "msda_backward_counters.json"),
 }
 KERNEL_SOURCES = {
     "forward": [os.path.join(CSRC, "msda_device.hpp"), os.path.join(CSRC, "msda_api.hip")],
     "forward_fused": [os.path.join(CSRC, "msda_device.hpp"), os.path.join(CSRC, "msda_api.hip")],
+    "forward_pruned": [os.path.join(CSRC, "msda_device.hpp"), os.path.join(CSRC, "msda_api.hip")],
     "backward": [os.path.join(CSRC, "msda_device.hpp"), os.path.join(CSRC, "msda_backward.hpp"),
                  os.path.join(CSRC, "msda_api.hip")],
 }
@@ -121,7 +128,7 @@ def counters_for(workload_name: str, op: str = "forward"):
     return entry.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(w, inp, max_points=60_000_000, grad_out=None):
+def cpu_baseline(w, inp, max_points=60_000_000, grad_out=None, threshold=None):
     """Time the oracle (single-threaded C) on the same inputs, bounded; the
     backward oracle when ``grad_out`` is given, the fused-front-end oracle when
     ``inp`` holds reference points, offsets and logits."""
@@ -133,6 +140,9 @@ def cpu_baseline(w, inp, max_points=60_000_000, grad_out=None):
     if fused:
         fn = (oracle.msda_oracle_forward_fused if w.dims == 2
               else oracle.msda3d_oracle_forward_fused)
+    elif threshold is not None:
+        fn = (oracle.msda_oracle_forward_pruned if w.dims == 2
+              else oracle.msda3d_oracle_forward_pruned)
     elif grad_out is None:
         fn = oracle.msda_oracle_forward if w.dims == 2 else oracle.msda3d_oracle_forward
     else:
@@ -158,6 +168,8 @@ def cpu_baseline(w, inp, max_points=60_000_000, grad_out=None):
         args = (value, shapes, starts, loc, attw)
     if grad_out is not None:
         args += (grad_out[:nb, :nq].double().numpy(),)
+    if threshold is not None:
+        args += (threshold,)
     t0 = time.perf_counter()
     fn(*args)
     dt = time.perf_counter() - t0
@@ -179,9 +191,14 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="detr_encoder",
                     help="workload name (default: the DETR encoder configuration)")
-    ap.add_argument("--op", choices=("forward", "forward_fused", "backward"), default="forward",
+    ap.add_argument("--op", choices=("forward", "forward_fused", "forward_pruned", "backward"),
+                    default="forward",
                     help="time the forward (default), the forward with the fused front "
-                         "end, or the backward entry point")
+                         "end, the pruned forward, or the backward entry point")
+    ap.add_argument("--prune-threshold", type=float, default=None,
+                    help="attention-weight threshold of --op forward_pruned "
+                         "(default 0.8 / (L*P): about half the samples of softmaxed "
+                         "N(0,1) logits)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip timing the oracle (for profiler runs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -198,8 +215,9 @@ def main(argv=None):
     import torch
 
     from scale_deformable_attention_02_amd import (msda3d_backward, msda3d_forward,
-                                                   msda3d_forward_fused, msda_backward,
-                                                   msda_forward, msda_forward_fused)
+                                                   msda3d_forward_fused, msda3d_forward_pruned,
+                                                   msda_backward, msda_forward,
+                                                   msda_forward_fused, msda_forward_pruned)
     from scale_deformable_attention_02_amd.workloads import (CONFIGS, make_fused_inputs,
                                                              make_grad_out, make_inputs)
 
@@ -207,6 +225,10 @@ def main(argv=None):
     dev = torch.device("cuda:0")
     backward = args.op == "backward"
     fused = args.op == "forward_fused"
+    pruned = args.op == "forward_pruned"
+    threshold = args.prune_threshold
+    if pruned and threshold is None:
+        threshold = 0.8 / (w.L * w.P)
     inp = make_fused_inputs(w) if fused else make_inputs(w)
     U, G = backward_byte_counts(w) if backward else byte_counts(w)
     if fused:  # plus the reference points, read once
@@ -248,6 +270,23 @@ def main(argv=None):
             attw = torch.softmax(d["attention_logits"].reshape(N, Lq, M, L * P), dim=-1)
             fwd(d["value"], d["spatial_shapes"], d["level_start_index"], loc,
                 attw.reshape(N, Lq, M, L, P), out=outs[i % copies])
+    elif pruned:
+        out_dt = torch.bfloat16 if w.out_dtype == "bf16" else torch.float32
+        outs = [torch.empty((w.N, w.queries_per_image, w.M * w.D), dtype=out_dt, device=dev)
+                for _ in range(copies)]
+        pfn = msda_forward_pruned if w.dims == 2 else msda3d_forward_pruned
+        fwd = msda_forward if w.dims == 2 else msda3d_forward
+
+        def step(i):
+            d = sets[i % copies]
+            pfn(d["value"], d["spatial_shapes"], d["level_start_index"],
+                d["sampling_locations"], d["attention_weights"], threshold,
+                out=outs[i % copies])
+
+        def unfused_step(i):  # the unpruned kernel on the same inputs
+            d = sets[i % copies]
+            fwd(d["value"], d["spatial_shapes"], d["level_start_index"],
+                d["sampling_locations"], d["attention_weights"], out=outs[i % copies])
     else:
         out_dt = torch.bfloat16 if w.out_dtype == "bf16" else torch.float32
         outs = [torch.empty((w.N, w.queries_per_image, w.M * w.D), dtype=out_dt, device=dev)
@@ -288,16 +327,20 @@ def main(argv=None):
     warm_s = statistics.median([a.elapsed_time(b) for a, b in warm_ev]) / 1e3
 
     unfused_us = None
-    if fused:
-        # the same work with the front end as separate torch passes
+    if fused or pruned:
+        # the comparison leg (fused: the front end as separate torch passes;
+        # pruned: the unpruned kernel), timed the same way as the main leg
         for i in range(3):
             unfused_step(i)
         torch.cuda.synchronize()
-        t1 = time.perf_counter()
+        cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
         for i in range(args.steps):
+            cev[i][0].record(stream)
             unfused_step(i)
+            cev[i][1].record(stream)
         torch.cuda.synchronize()
-        unfused_us = (time.perf_counter() - t1) / args.steps * 1e6
+        unfused_us = statistics.mean(a.elapsed_time(b) for a, b in cev) * 1e3
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib << 20
@@ -313,7 +356,8 @@ def main(argv=None):
     achieved = U / kernel_s / 1e9
     traffic = counters_for(w.name, args.op)
     result = {
-        "metric": METRIC_BACKWARD if backward else (METRIC_FUSED if fused else METRIC),
+        "metric": (METRIC_BACKWARD if backward else METRIC_FUSED if fused
+                   else METRIC_PRUNED if pruned else METRIC),
         "value": points / (wall / args.steps),
         "unit": "sampled points/s",
         "n_gpus": 1,
@@ -338,7 +382,15 @@ def main(argv=None):
         "kernel_us_median": statistics.median(launch_ms) * 1e3,
         "kernel_us_warm_median": warm_s * 1e6,
         "bytes_per_launch": {"compulsory": U, "gathered": G},
-        "unfused_pipeline_us_per_step": unfused_us,
+        "unfused_pipeline_us_per_step": unfused_us if fused else None,
+        "unpruned_us_per_step": unfused_us if pruned else None,
+        "prune": ({"threshold": threshold,
+                   "pruned_fraction": float((inp["attention_weights"] < threshold).double().mean()),
+                   "pruned_weight_mass": float(
+                       torch.where(inp["attention_weights"] < threshold,
+                                   inp["attention_weights"], 0).double().sum()
+                       / inp["attention_weights"].double().sum())}
+                  if pruned else None),
         "roofline": {
             "bound": "hbm",
             "achieved": achieved,
@@ -350,7 +402,8 @@ def main(argv=None):
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(
-            w, inp, grad_out=make_grad_out(w) if backward else None)
+            w, inp, grad_out=make_grad_out(w) if backward else None,
+            threshold=threshold if pruned else None)
     print(json.dumps(result), flush=True)
     return 0
 

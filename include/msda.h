@@ -117,6 +117,38 @@ int msda3d_forward(const void* value, int value_dtype,
                    int64_t Lq, int64_t L, int64_t P, void* stream);
 
 /*
+ * 2D forward with probability-aware point pruning (DEFA, abstract: sampling
+ * points pruned by their probability): a sample whose attention weight is
+ * below `threshold` contributes nothing; every other sample contributes
+ * exactly as in msda_forward, with its weight unchanged (no renormalisation).
+ * The test is `weight < threshold` in fp32, so NaN weights are kept and
+ * -INFINITY keeps every sample.  Kept samples are packed before their corners
+ * are gathered, so the work shrinks with the pruned fraction.  The result
+ * equals msda_forward's on the weights with the pruned ones set to 0.
+ * Arguments, limits and errors are msda_forward's.
+ */
+int msda_forward_pruned(const void* value, int value_dtype,
+                        const int64_t* spatial_shapes,
+                        const int64_t* level_start_index,
+                        const float* sampling_locations,
+                        const float* attention_weights,
+                        float threshold,
+                        void* out, int out_dtype,
+                        int64_t N, int64_t S, int64_t M, int64_t D,
+                        int64_t Lq, int64_t L, int64_t P, void* stream);
+
+/* 3D counterpart of msda_forward_pruned. */
+int msda3d_forward_pruned(const void* value, int value_dtype,
+                          const int64_t* spatial_shapes,
+                          const int64_t* level_start_index,
+                          const float* sampling_locations,
+                          const float* attention_weights,
+                          float threshold,
+                          void* out, int out_dtype,
+                          int64_t N, int64_t S, int64_t M, int64_t D,
+                          int64_t Lq, int64_t L, int64_t P, void* stream);
+
+/*
  * 2D forward with the module's front end fused into the kernel.  Instead of
  * sampling_locations and attention_weights it takes
  *   reference_points   float [N][Lq][2]            (x, y), normalized

@@ -16,6 +16,8 @@ sampling locations and attention weights for a given ``grad_out``.
 ``msda_oracle_forward_fused`` and ``msda3d_oracle_forward_fused`` add the
 module's front end: softmax of attention logits (fp64) and location =
 reference point + offset (fp32), then the same forward.
+``msda_oracle_forward_pruned`` / ``msda3d_oracle_forward_pruned`` drop the
+samples whose attention weight is below a threshold.
 """
 from __future__ import annotations
 
@@ -58,6 +60,10 @@ def _load():
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [ptr] * 9 + [i64] * 7
+    for name in ("msda_oracle_forward_pruned", "msda3d_oracle_forward_pruned"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [ptr] * 5 + [ctypes.c_double, ptr] + [i64] * 7
     for name in ("msda_oracle_forward_fused", "msda3d_oracle_forward_fused"):
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
@@ -86,7 +92,7 @@ def _as_numpy(x, dtype):
 
 
 def _run(dims, value, spatial_shapes, level_start_index, sampling_locations,
-         attention_weights):
+         attention_weights, threshold=None):
     lib = _load()
     v = _as_numpy(value, np.float64)
     shapes = _as_numpy(spatial_shapes, np.int64)
@@ -102,9 +108,15 @@ def _run(dims, value, spatial_shapes, level_start_index, sampling_locations,
     if aw.shape != loc.shape[:-1] or shapes.shape != (L, dims) or lsi.shape != (L,):
         raise ValueError("inconsistent shapes")
     out = np.empty((N, Lq, M * D), dtype=np.float64)
-    fn = lib.msda_oracle_forward if dims == 2 else lib.msda3d_oracle_forward
-    rc = fn(v.ctypes.data, shapes.ctypes.data, lsi.ctypes.data, loc.ctypes.data,
-            aw.ctypes.data, out.ctypes.data, N, S, M, D, Lq, L, P)
+    if threshold is None:
+        fn = lib.msda_oracle_forward if dims == 2 else lib.msda3d_oracle_forward
+        rc = fn(v.ctypes.data, shapes.ctypes.data, lsi.ctypes.data, loc.ctypes.data,
+                aw.ctypes.data, out.ctypes.data, N, S, M, D, Lq, L, P)
+    else:
+        fn = lib.msda_oracle_forward_pruned if dims == 2 else lib.msda3d_oracle_forward_pruned
+        thr = float(np.float32(threshold))   # the threshold is an fp32 value
+        rc = fn(v.ctypes.data, shapes.ctypes.data, lsi.ctypes.data, loc.ctypes.data,
+                aw.ctypes.data, thr, out.ctypes.data, N, S, M, D, Lq, L, P)
     if rc != 0:
         raise ValueError(f"oracle rejected its arguments (code {rc})")
     return out
@@ -148,6 +160,21 @@ def msda3d_oracle_backward(value, spatial_shapes, level_start_index, sampling_lo
     """3D backward (trilinear); see msda_oracle_backward."""
     return _run_backward(3, value, spatial_shapes, level_start_index, sampling_locations,
                          attention_weights, grad_out)
+
+
+def msda_oracle_forward_pruned(value, spatial_shapes, level_start_index, sampling_locations,
+                               attention_weights, threshold) -> np.ndarray:
+    """2D forward dropping samples whose attention weight is below ``threshold``
+    (rounded to fp32); the kept weights are used as given."""
+    return _run(2, value, spatial_shapes, level_start_index, sampling_locations,
+                attention_weights, threshold)
+
+
+def msda3d_oracle_forward_pruned(value, spatial_shapes, level_start_index, sampling_locations,
+                                 attention_weights, threshold) -> np.ndarray:
+    """3D counterpart of ``msda_oracle_forward_pruned``."""
+    return _run(3, value, spatial_shapes, level_start_index, sampling_locations,
+                attention_weights, threshold)
 
 
 def msda_oracle_forward(value, spatial_shapes, level_start_index,

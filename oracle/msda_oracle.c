@@ -44,12 +44,11 @@ static int check_levels(const int64_t* shapes, const int64_t* start, int64_t L,
  * recipe step 3), weighted by A and summed over levels and points into one
  * sum per (n, q, m) ("Deformable Attention Module" equation, inner bracket;
  * "3D Attention...", multi-scale L x P sum). */
-int msda_oracle_forward(const double* value, const int64_t* spatial_shapes,
-                        const int64_t* level_start_index,
-                        const float* sampling_locations,
-                        const double* attention_weights, double* out,
-                        int64_t N, int64_t S, int64_t M, int64_t D,
-                        int64_t Lq, int64_t L, int64_t P) {
+static int forward2d(const double* value, const int64_t* spatial_shapes,
+                     const int64_t* level_start_index, const float* sampling_locations,
+                     const double* attention_weights, double threshold, double* out,
+                     int64_t N, int64_t S, int64_t M, int64_t D,
+                     int64_t Lq, int64_t L, int64_t P) {
     if (N < 0 || S < 0 || M < 0 || D < 0 || Lq < 0 || L < 0 || P < 0) return 2;
     if (N == 0 || Lq == 0 || M == 0 || D == 0) return 0;
     if (!value || !spatial_shapes || !level_start_index || !sampling_locations ||
@@ -70,6 +69,7 @@ int msda_oracle_forward(const double* value, const int64_t* spatial_shapes,
                     for (int64_t p = 0; p < P; ++p) {
                         const int64_t k = (((n * Lq + q) * M + m) * L + l) * P + p;
                         const double a = attention_weights[k];
+                        if (a < threshold) continue;  /* pruned sample */
                         const float x = sampling_locations[2 * k + 0];
                         const float y = sampling_locations[2 * k + 1];
 
@@ -109,12 +109,11 @@ int msda_oracle_forward(const double* value, const int64_t* spatial_shapes,
 /* 3D: the same sum with (x, y, z) locations, (Z, H, W) level shapes and
  * trilinear interpolation over the 8 corners of the voxel cube around the
  * point ("3D Attention That Knows Where to Look", 2D->3D change list). */
-int msda3d_oracle_forward(const double* value, const int64_t* spatial_shapes,
-                          const int64_t* level_start_index,
-                          const float* sampling_locations,
-                          const double* attention_weights, double* out,
-                          int64_t N, int64_t S, int64_t M, int64_t D,
-                          int64_t Lq, int64_t L, int64_t P) {
+static int forward3d(const double* value, const int64_t* spatial_shapes,
+                     const int64_t* level_start_index, const float* sampling_locations,
+                     const double* attention_weights, double threshold, double* out,
+                     int64_t N, int64_t S, int64_t M, int64_t D,
+                     int64_t Lq, int64_t L, int64_t P) {
     if (N < 0 || S < 0 || M < 0 || D < 0 || Lq < 0 || L < 0 || P < 0) return 2;
     if (N == 0 || Lq == 0 || M == 0 || D == 0) return 0;
     if (!value || !spatial_shapes || !level_start_index || !sampling_locations ||
@@ -136,6 +135,7 @@ int msda3d_oracle_forward(const double* value, const int64_t* spatial_shapes,
                     for (int64_t p = 0; p < P; ++p) {
                         const int64_t k = (((n * Lq + q) * M + m) * L + l) * P + p;
                         const double a = attention_weights[k];
+                        if (a < threshold) continue;  /* pruned sample */
                         const float x = sampling_locations[3 * k + 0];
                         const float y = sampling_locations[3 * k + 1];
                         const float z = sampling_locations[3 * k + 2];
@@ -183,6 +183,51 @@ int msda3d_oracle_forward(const double* value, const int64_t* spatial_shapes,
         }
     }
     return 0;
+}
+
+int msda_oracle_forward(const double* value, const int64_t* spatial_shapes,
+                        const int64_t* level_start_index,
+                        const float* sampling_locations,
+                        const double* attention_weights, double* out,
+                        int64_t N, int64_t S, int64_t M, int64_t D,
+                        int64_t Lq, int64_t L, int64_t P) {
+    return forward2d(value, spatial_shapes, level_start_index, sampling_locations,
+                     attention_weights, -INFINITY, out, N, S, M, D, Lq, L, P);
+}
+
+int msda3d_oracle_forward(const double* value, const int64_t* spatial_shapes,
+                          const int64_t* level_start_index,
+                          const float* sampling_locations,
+                          const double* attention_weights, double* out,
+                          int64_t N, int64_t S, int64_t M, int64_t D,
+                          int64_t Lq, int64_t L, int64_t P) {
+    return forward3d(value, spatial_shapes, level_start_index, sampling_locations,
+                     attention_weights, -INFINITY, out, N, S, M, D, Lq, L, P);
+}
+
+/* Probability-aware point pruning (DEFA, abstract: sampling points are pruned
+ * by their probability): a sample whose attention weight is below `threshold`
+ * is dropped, the others are kept with their weights unchanged (no
+ * renormalisation).  The comparison is on the given fp32 weight, widened
+ * exactly; NaN weights are kept. */
+int msda_oracle_forward_pruned(const double* value, const int64_t* spatial_shapes,
+                               const int64_t* level_start_index,
+                               const float* sampling_locations,
+                               const double* attention_weights, double threshold,
+                               double* out, int64_t N, int64_t S, int64_t M, int64_t D,
+                               int64_t Lq, int64_t L, int64_t P) {
+    return forward2d(value, spatial_shapes, level_start_index, sampling_locations,
+                     attention_weights, threshold, out, N, S, M, D, Lq, L, P);
+}
+
+int msda3d_oracle_forward_pruned(const double* value, const int64_t* spatial_shapes,
+                                 const int64_t* level_start_index,
+                                 const float* sampling_locations,
+                                 const double* attention_weights, double threshold,
+                                 double* out, int64_t N, int64_t S, int64_t M, int64_t D,
+                                 int64_t Lq, int64_t L, int64_t P) {
+    return forward3d(value, spatial_shapes, level_start_index, sampling_locations,
+                     attention_weights, threshold, out, N, S, M, D, Lq, L, P);
 }
 
 /* Backward, 2D.  For each sample the forward is

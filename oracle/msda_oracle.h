@@ -107,6 +107,26 @@ int msda3d_oracle_backward(const double* value, const int64_t* spatial_shapes,
                            int64_t Lq, int64_t L, int64_t P);
 
 /*
+ * Forward with probability-aware point pruning: a sample whose attention
+ * weight is below `threshold` (the fp32 weight widened exactly; threshold
+ * given as a double holding an fp32 value) contributes nothing; the other
+ * weights are used unchanged.  NaN weights are kept.  -INFINITY keeps all.
+ */
+int msda_oracle_forward_pruned(const double* value, const int64_t* spatial_shapes,
+                               const int64_t* level_start_index,
+                               const float* sampling_locations,
+                               const double* attention_weights, double threshold,
+                               double* out, int64_t N, int64_t S, int64_t M, int64_t D,
+                               int64_t Lq, int64_t L, int64_t P);
+
+int msda3d_oracle_forward_pruned(const double* value, const int64_t* spatial_shapes,
+                                 const int64_t* level_start_index,
+                                 const float* sampling_locations,
+                                 const double* attention_weights, double threshold,
+                                 double* out, int64_t N, int64_t S, int64_t M, int64_t D,
+                                 int64_t Lq, int64_t L, int64_t P);
+
+/*
  * Forward with the module's front end: attention weights are the softmax over
  * the L*P samples of each (n, q, m) of attention_logits (double, widened from
  * fp32), computed in fp64; sampling location = reference_points[n][q] +

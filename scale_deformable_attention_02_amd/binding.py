@@ -1,8 +1,8 @@
 """Python binding of the C ABI in ``include/msda.h`` (argument marshalling only).
 
-``msda_forward`` / ``msda3d_forward``, ``msda_forward_fused`` /
-``msda3d_forward_fused`` and ``msda_backward`` / ``msda3d_backward`` take
-torch tensors that already live on the GPU, check
+``msda_forward`` / ``msda3d_forward``, ``msda_forward_pruned`` /
+``msda3d_forward_pruned``, ``msda_forward_fused`` / ``msda3d_forward_fused``
+and ``msda_backward`` / ``msda3d_backward`` take torch tensors that already live on the GPU, check
 dtypes/shapes/contiguity, allocate outputs with torch when the caller passes
 none, and call the same-named C entry point of ``libmsda.so`` on torch's
 current HIP stream.  Every step of the computation
@@ -34,8 +34,9 @@ STATUS = {
 }
 
 # Every symbol include/msda.h declares.
-EXPORTED = ("msda_forward", "msda3d_forward", "msda_forward_fused", "msda3d_forward_fused",
-            "msda_backward", "msda3d_backward", "msda_status_string")
+EXPORTED = ("msda_forward", "msda3d_forward", "msda_forward_pruned", "msda3d_forward_pruned",
+            "msda_forward_fused", "msda3d_forward_fused", "msda_backward", "msda3d_backward",
+            "msda_status_string")
 
 _lib = None
 
@@ -69,6 +70,11 @@ def load_library() -> ctypes.CDLL:
         fn.restype = ctypes.c_int
         fn.argtypes = [vp, ctypes.c_int, vp, vp, vp, vp, vp, ctypes.c_int,
                        i64, i64, i64, i64, i64, i64, i64, vp]
+    for name in ("msda_forward_pruned", "msda3d_forward_pruned"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [vp, ctypes.c_int, vp, vp, vp, vp, ctypes.c_float, vp, ctypes.c_int,
+                       i64, i64, i64, i64, i64, i64, i64, vp]
     for name in ("msda_forward_fused", "msda3d_forward_fused"):
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
@@ -97,6 +103,17 @@ def raw_call(dims: int, value_ptr: int, value_dtype: int, shapes_ptr: int,
     lib = load_library()
     fn = lib.msda_forward if dims == 2 else lib.msda3d_forward
     return fn(value_ptr, value_dtype, shapes_ptr, starts_ptr, loc_ptr, attw_ptr,
+              out_ptr, out_dtype, N, S, M, D, Lq, L, P, stream)
+
+
+def raw_pruned_call(dims: int, value_ptr: int, value_dtype: int, shapes_ptr: int,
+                    starts_ptr: int, loc_ptr: int, attw_ptr: int, threshold: float, out_ptr: int,
+                    out_dtype: int, N: int, S: int, M: int, D: int, Lq: int, L: int, P: int,
+                    stream: int = 0) -> int:
+    """Call the pruned forward with raw pointers; returns the msda_status."""
+    lib = load_library()
+    fn = lib.msda_forward_pruned if dims == 2 else lib.msda3d_forward_pruned
+    return fn(value_ptr, value_dtype, shapes_ptr, starts_ptr, loc_ptr, attw_ptr, threshold,
               out_ptr, out_dtype, N, S, M, D, Lq, L, P, stream)
 
 
@@ -166,7 +183,8 @@ def _forward(dims: int, value: torch.Tensor, spatial_shapes: torch.Tensor,
              level_start_index: torch.Tensor, sampling_locations: torch.Tensor,
              attention_weights: torch.Tensor, out: Optional[torch.Tensor],
              out_dtype: Optional[torch.dtype],
-             stream: Optional[torch.cuda.Stream]) -> torch.Tensor:
+             stream: Optional[torch.cuda.Stream],
+             threshold: Optional[float] = None) -> torch.Tensor:
     code, N, S, M, D, Lq, L, P = _check_inputs(dims, value, spatial_shapes, level_start_index,
                                                sampling_locations, attention_weights)
     if out is None:
@@ -177,10 +195,16 @@ def _forward(dims: int, value: torch.Tensor, spatial_shapes: torch.Tensor,
         raise ValueError("out must be a contiguous [N, Lq, M*D] tensor on value's device")
     out_code = _dtype_code(out.dtype, "out")
     s = stream if stream is not None else torch.cuda.current_stream(value.device)
-    status = raw_call(dims, value.data_ptr(), code, spatial_shapes.data_ptr(),
-                      level_start_index.data_ptr(), sampling_locations.data_ptr(),
-                      attention_weights.data_ptr(), out.data_ptr(), out_code,
-                      N, S, M, D, Lq, L, P, s.cuda_stream)
+    if threshold is None:
+        status = raw_call(dims, value.data_ptr(), code, spatial_shapes.data_ptr(),
+                          level_start_index.data_ptr(), sampling_locations.data_ptr(),
+                          attention_weights.data_ptr(), out.data_ptr(), out_code,
+                          N, S, M, D, Lq, L, P, s.cuda_stream)
+    else:
+        status = raw_pruned_call(dims, value.data_ptr(), code, spatial_shapes.data_ptr(),
+                                 level_start_index.data_ptr(), sampling_locations.data_ptr(),
+                                 attention_weights.data_ptr(), float(threshold), out.data_ptr(),
+                                 out_code, N, S, M, D, Lq, L, P, s.cuda_stream)
     if status != 0:
         raise MsdaError(status, status_string(status))
     return out
@@ -261,6 +285,25 @@ def msda3d_backward(value, spatial_shapes, level_start_index, sampling_locations
     return _backward(3, value, spatial_shapes, level_start_index, sampling_locations,
                      attention_weights, grad_out, grad_value, grad_sampling_locations,
                      grad_attention_weights, stream)
+
+
+def msda_forward_pruned(value, spatial_shapes, level_start_index, sampling_locations,
+                        attention_weights, threshold, out=None, out_dtype=None,
+                        stream=None) -> torch.Tensor:
+    """2D MSDA forward with probability-aware point pruning: samples whose
+    attention weight is below ``threshold`` (an fp32 value) are skipped, the
+    others keep their weights (no renormalisation); otherwise as
+    ``msda_forward``."""
+    return _forward(2, value, spatial_shapes, level_start_index, sampling_locations,
+                    attention_weights, out, out_dtype, stream, threshold)
+
+
+def msda3d_forward_pruned(value, spatial_shapes, level_start_index, sampling_locations,
+                          attention_weights, threshold, out=None, out_dtype=None,
+                          stream=None) -> torch.Tensor:
+    """3D counterpart of ``msda_forward_pruned``."""
+    return _forward(3, value, spatial_shapes, level_start_index, sampling_locations,
+                    attention_weights, out, out_dtype, stream, threshold)
 
 
 def _forward_fused(dims, value, spatial_shapes, level_start_index, reference_points,

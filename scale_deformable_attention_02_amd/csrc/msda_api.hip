@@ -53,32 +53,34 @@ int ceil_log2(int64_t x) {
     return r;
 }
 
-template <typename TV, typename TO, int DIM, int CPL, bool FUSED>
+// Variants: plain forward, fused front end, pruned forward (never both).
+template <typename TV, typename TO, int DIM, int CPL, bool FUSED, bool PRUNE>
 void launch_one(const Params& p, hipStream_t stream) {
-    hipLaunchKernelGGL((msda::msda_forward_kernel<TV, TO, DIM, CPL, FUSED>), dim3(p.num_blocks),
-                       dim3(msda::kBlockThreads), 0, stream, p);
+    hipLaunchKernelGGL((msda::msda_forward_kernel<TV, TO, DIM, CPL, FUSED, PRUNE>),
+                       dim3(p.num_blocks), dim3(msda::kBlockThreads), 0, stream, p);
 }
 
-template <typename TV, typename TO, int DIM, int CPL, bool FUSED>
+template <typename TV, typename TO, int DIM, int CPL, bool FUSED, bool PRUNE>
 void launch_staged_one(const StagedParams& sp, hipStream_t stream) {
     static_assert(MSDA_STAGE_BUDGET <= 64 * 1024, "dynamic LDS above the default limit");
     if constexpr (DIM == 2)  // the staged kernel is only launched for 2D pyramids
-        hipLaunchKernelGGL((msda::msda_forward_staged_kernel<TV, TO, DIM, CPL, FUSED>),
+        hipLaunchKernelGGL((msda::msda_forward_staged_kernel<TV, TO, DIM, CPL, FUSED, PRUNE>),
                            dim3(sp.p.num_blocks), dim3(msda::kStagedThreads), sp.stage_bytes,
                            stream, sp);
 }
 
 // Kernel selection by CPL (lanes per head row), then by value/out type.
-template <typename TV, typename TO, int DIM, bool FUSED, typename P>
+template <typename TV, typename TO, int DIM, bool FUSED, bool PRUNE, typename P>
 void launch_cpl(int cpl, const P& p, hipStream_t stream) {
+    static_assert(!(FUSED && PRUNE), "no fused and pruned variant");
     constexpr bool staged = std::is_same<P, StagedParams>::value;
     switch (cpl) {
-#define MSDA_CASE(C)                                             \
-    case C:                                                      \
-        if constexpr (staged)                                    \
-            launch_staged_one<TV, TO, DIM, C, FUSED>(p, stream); \
-        else                                                     \
-            launch_one<TV, TO, DIM, C, FUSED>(p, stream);        \
+#define MSDA_CASE(C)                                                    \
+    case C:                                                             \
+        if constexpr (staged)                                           \
+            launch_staged_one<TV, TO, DIM, C, FUSED, PRUNE>(p, stream); \
+        else                                                            \
+            launch_one<TV, TO, DIM, C, FUSED, PRUNE>(p, stream);        \
         break;
         MSDA_CASE(1)
         MSDA_CASE(2)
@@ -88,26 +90,26 @@ void launch_cpl(int cpl, const P& p, hipStream_t stream) {
         MSDA_CASE(32)
         default:
             if constexpr (staged)
-                launch_staged_one<TV, TO, DIM, 64, FUSED>(p, stream);
+                launch_staged_one<TV, TO, DIM, 64, FUSED, PRUNE>(p, stream);
             else
-                launch_one<TV, TO, DIM, 64, FUSED>(p, stream);
+                launch_one<TV, TO, DIM, 64, FUSED, PRUNE>(p, stream);
             break;
 #undef MSDA_CASE
     }
 }
 
-template <int DIM, bool FUSED, typename P>
+template <int DIM, bool FUSED, bool PRUNE, typename P>
 void launch(int value_dtype, int out_dtype, int cpl, const P& p, hipStream_t stream) {
     if (value_dtype == MSDA_F32) {
         if (out_dtype == MSDA_F32)
-            launch_cpl<float, float, DIM, FUSED>(cpl, p, stream);
+            launch_cpl<float, float, DIM, FUSED, PRUNE>(cpl, p, stream);
         else
-            launch_cpl<float, msda::Bf16, DIM, FUSED>(cpl, p, stream);
+            launch_cpl<float, msda::Bf16, DIM, FUSED, PRUNE>(cpl, p, stream);
     } else {
         if (out_dtype == MSDA_F32)
-            launch_cpl<msda::Bf16, float, DIM, FUSED>(cpl, p, stream);
+            launch_cpl<msda::Bf16, float, DIM, FUSED, PRUNE>(cpl, p, stream);
         else
-            launch_cpl<msda::Bf16, msda::Bf16, DIM, FUSED>(cpl, p, stream);
+            launch_cpl<msda::Bf16, msda::Bf16, DIM, FUSED, PRUNE>(cpl, p, stream);
     }
 }
 
@@ -118,13 +120,15 @@ bool aligned(const void* ptr, uintptr_t a) {
 }
 
 // FUSED: sampling_locations holds the offsets, attention_weights the logits,
-// and reference_points [N][Lq][DIM] the reference points.
-template <int DIM, bool FUSED>
+// and reference_points [N][Lq][DIM] the reference points.  PRUNE: samples
+// with attention weight below prune_threshold are dropped.
+template <int DIM, bool FUSED, bool PRUNE = false>
 int forward(const void* value, int value_dtype, const int64_t* spatial_shapes,
             const int64_t* level_start_index, const float* sampling_locations,
             const float* attention_weights, void* out, int out_dtype, int64_t N,
             int64_t S, int64_t M, int64_t D, int64_t Lq, int64_t L, int64_t P,
-            void* stream, const float* reference_points = nullptr) {
+            void* stream, const float* reference_points = nullptr,
+            float prune_threshold = 0.0f) {
     if (N < 0 || Lq < 0 || S < 1 || M < 1 || D < 1 || L < 1 || P < 1)
         return MSDA_ERR_DIM;
     if (!known_dtype(value_dtype) || !known_dtype(out_dtype)) return MSDA_ERR_DTYPE;
@@ -227,6 +231,7 @@ int forward(const void* value, int value_dtype, const int64_t* spatial_shapes,
                 p.ref = reference_points + (n0 * Lq + q0) * DIM;
                 p.ref_bytes = static_cast<uint32_t>(nbatch * nquery * DIM * 4);
             }
+            p.prune = prune_threshold;
 
             // Staged kernel: large 2D launches whose phase-B iterations are
             // level-pure (G divides P), with MSDA_STAGED_WGS_PER_SLICE
@@ -251,12 +256,12 @@ int forward(const void* value, int value_dtype, const int64_t* spatial_shapes,
                 sp.div_wgs = make_fast_div(static_cast<uint32_t>(wgs_per_slice));
                 sp.stage_bytes = static_cast<uint32_t>(stage);
                 sp.ipl = static_cast<int32_t>(P / G);
-                launch<DIM, FUSED>(value_dtype, out_dtype, cpl, sp, hs);
+                launch<DIM, FUSED, PRUNE>(value_dtype, out_dtype, cpl, sp, hs);
                 if (hipGetLastError() != hipSuccess) return MSDA_ERR_LAUNCH;
                 continue;
             }
 
-            launch<DIM, FUSED>(value_dtype, out_dtype, cpl, p, hs);
+            launch<DIM, FUSED, PRUNE>(value_dtype, out_dtype, cpl, p, hs);
             if (hipGetLastError() != hipSuccess) return MSDA_ERR_LAUNCH;
         }
     }
@@ -455,6 +460,26 @@ int msda3d_forward(const void* value, int value_dtype, const int64_t* spatial_sh
     return forward<3, false>(value, value_dtype, spatial_shapes, level_start_index,
                              sampling_locations, attention_weights, out, out_dtype, N, S, M, D,
                              Lq, L, P, stream);
+}
+
+int msda_forward_pruned(const void* value, int value_dtype, const int64_t* spatial_shapes,
+                        const int64_t* level_start_index, const float* sampling_locations,
+                        const float* attention_weights, float threshold, void* out,
+                        int out_dtype, int64_t N, int64_t S, int64_t M, int64_t D, int64_t Lq,
+                        int64_t L, int64_t P, void* stream) {
+    return forward<2, false, true>(value, value_dtype, spatial_shapes, level_start_index,
+                                   sampling_locations, attention_weights, out, out_dtype, N, S,
+                                   M, D, Lq, L, P, stream, nullptr, threshold);
+}
+
+int msda3d_forward_pruned(const void* value, int value_dtype, const int64_t* spatial_shapes,
+                          const int64_t* level_start_index, const float* sampling_locations,
+                          const float* attention_weights, float threshold, void* out,
+                          int out_dtype, int64_t N, int64_t S, int64_t M, int64_t D,
+                          int64_t Lq, int64_t L, int64_t P, void* stream) {
+    return forward<3, false, true>(value, value_dtype, spatial_shapes, level_start_index,
+                                   sampling_locations, attention_weights, out, out_dtype, N, S,
+                                   M, D, Lq, L, P, stream, nullptr, threshold);
 }
 
 int msda_forward_fused(const void* value, int value_dtype, const int64_t* spatial_shapes,

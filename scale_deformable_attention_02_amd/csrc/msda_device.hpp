@@ -110,6 +110,8 @@ struct Params {
     // the reference points, at (n0, q0): rows (n*Lq + q) of DIM floats
     const float* ref;
     uint32_t ref_bytes;
+    // pruned forward only: samples with attention weight below this are dropped
+    float prune;
 };
 
 // One sample's contribution recipe: NC corner byte offsets (relative to the
@@ -453,11 +455,48 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Probability-aware pruning: lanes i*NG + g (i = 0, 1, ...) hold the samples
+// of point group g.  Kept samples are packed, in order, to the front of their
+// group's list, so phase B runs max-over-groups iterations instead of NI.
+// Lane masks of one group: bits g, g + NG, g + 2 NG, ...
+template <int NG>
+__device__ __forceinline__ uint64_t group_lanes(int g) {
+    constexpr uint64_t rep = NG >= 64 ? 1ull : ~0ull / ((1ull << NG) - 1ull);
+    return rep << g;
+}
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
+#pragma unroll
+    for (int b = 1; b < kWave; b <<= 1) x = max(x, static_cast<uint32_t>(__shfl_xor(static_cast<int>(x), b, kWave)));
+    return x;
+}
+
+// Rank of this lane among the kept lanes of its group (lanes below it), and
+// the group's kept count.
+template <int NG>
+__device__ __forceinline__ void group_rank(uint64_t kept, int lane, int g, uint32_t& rank,
+                                           uint32_t& count) {
+    const uint64_t mine = kept & group_lanes<NG>(g);
+    rank = static_cast<uint32_t>(__popcll(mine & ((1ull << lane) - 1ull)));
+    count = static_cast<uint32_t>(__popcll(mine));
+}
+
+template <int NC>
+__device__ __forceinline__ Slot<NC> dead_slot(uint32_t invalid) {
+    Slot<NC> sl;
+#pragma unroll
+    for (int k = 0; k < NC; ++k) {
+        sl.off[k] = invalid;
+        sl.w[k] = 0.0f;
+    }
+    return sl;
+}
+
 // ---------------------------------------------------------------------------
 // Direct kernel: one pass of T tiles per wave, every corner gathered from HBM
 // (through L2/L1).  Used for small problems and as the general path.
 // ---------------------------------------------------------------------------
-template <typename TV, typename TO, int DIM, int CPL, bool FUSED = false>
+template <typename TV, typename TO, int DIM, int CPL, bool FUSED = false, bool PRUNE = false>
 __global__ __launch_bounds__(kBlockThreads) void msda_forward_kernel(Params p) {
     constexpr int NC = DIM == 2 ? 4 : 8;     // corners per sample
     constexpr int NG = kWave / CPL;          // point groups per wave
@@ -490,6 +529,7 @@ __global__ __launch_bounds__(kBlockThreads) void msda_forward_kernel(Params p) {
     const int G = 1 << p.log2G;
 
     // ---- Phase A: lane k fills slot k = i*NG + g (iteration i of group g).
+    int ni_run = p.NI;  // phase-B iterations (fewer when pruned samples are packed out)
     {
         const int i = lane / NG, g = lane % NG;
         const int t = g >> p.log2G, j = g & (G - 1);
@@ -512,8 +552,20 @@ __global__ __launch_bounds__(kBlockThreads) void msda_forward_kernel(Params p) {
 
         __syncthreads();  // smeta is ready
         const LevelGeom lg = smeta[s_c];
-        slots[wave][lane] = make_slot<DIM>(xyz, a, live, lg, head_base + lg.start_bytes,
+        const Slot<NC> sl = make_slot<DIM>(xyz, a, live, lg, head_base + lg.start_bytes,
                                            p.row_bytes, kOutOfRange);
+        if constexpr (PRUNE) {
+            const bool keep = live && !(a < p.prune);
+            const uint64_t kept = __ballot(keep);
+            uint32_t rank, count;
+            group_rank<NG>(kept, lane, g, rank, count);
+            ni_run = static_cast<int>(__builtin_amdgcn_readfirstlane(wave_max(count)));
+            slots[wave][lane] = dead_slot<NC>(kOutOfRange);
+            wave_lds_sync();
+            if (keep) slots[wave][rank * NG + g] = sl;
+        } else {
+            slots[wave][lane] = sl;
+        }
     }
     __syncthreads();
 
@@ -527,7 +579,7 @@ __global__ __launch_bounds__(kBlockThreads) void msda_forward_kernel(Params p) {
     float acc[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) acc[e] = 0.0f;
-    gather_hbm<TV, NC, NG, VEC>(buffer_of(p.value, p.value_bytes), &slots[wave][g], 0, p.NI,
+    gather_hbm<TV, NC, NG, VEC>(buffer_of(p.value, p.value_bytes), &slots[wave][g], 0, ni_run,
                                 lane_off, acc);
 
     const bool store = j == 0 && c < p.nchunk && wave_live &&
@@ -560,7 +612,7 @@ struct StagedParams {
     int32_t ipl;             // phase-B iterations per level, P / G
 };
 
-template <typename TV, typename TO, int DIM, int CPL, bool FUSED = false>
+template <typename TV, typename TO, int DIM, int CPL, bool FUSED = false, bool PRUNE = false>
 __global__ __launch_bounds__(kStagedThreads) void msda_forward_staged_kernel(StagedParams sp) {
     constexpr int NC = DIM == 2 ? 4 : 8;
     constexpr int NG = kWave / CPL;
@@ -700,7 +752,26 @@ __global__ __launch_bounds__(kStagedThreads) void msda_forward_staged_kernel(Sta
 
         // ---- Phase A
         if constexpr (FUSED) finish_sample_fused<DIM, ilog2<NG>()>(live, p.log2G, xyz, a, ref);
-        slots[wave][lane] = make_slot<DIM>(xyz, a, live, lga, slot_base, slot_stride, slot_invalid);
+        const Slot<NC> sl = make_slot<DIM>(xyz, a, live, lga, slot_base, slot_stride, slot_invalid);
+        int hbm_end = ni_hbm, lds_end = NI;
+        if constexpr (PRUNE) {
+            // pack kept samples within each segment (HBM levels, then LDS levels)
+            const bool keep = live && !(a < p.prune);
+            const bool in_hbm = ia < ni_hbm;
+            const uint64_t kept_hbm = __ballot(keep && in_hbm);
+            const uint64_t kept_lds = __ballot(keep && !in_hbm);
+            uint32_t rank_h, count_h, rank_l, count_l;
+            group_rank<NG>(kept_hbm, lane, ga, rank_h, count_h);
+            group_rank<NG>(kept_lds, lane, ga, rank_l, count_l);
+            hbm_end = static_cast<int>(__builtin_amdgcn_readfirstlane(wave_max(count_h)));
+            lds_end = hbm_end + static_cast<int>(__builtin_amdgcn_readfirstlane(wave_max(count_l)));
+            slots[wave][lane] = dead_slot<NC>(ia < hbm_end ? kOutOfRange : 0u);
+            wave_lds_sync();
+            if (keep)
+                slots[wave][(in_hbm ? rank_h : hbm_end + rank_l) * NG + ga] = sl;
+        } else {
+            slots[wave][lane] = sl;
+        }
         const uint32_t q_this = q0;
         q0 += stride;
         if (qc + stride < qb) {
@@ -714,8 +785,8 @@ __global__ __launch_bounds__(kStagedThreads) void msda_forward_staged_kernel(Sta
 #pragma unroll
         for (int e = 0; e < VEC; ++e) acc[e] = 0.0f;
         const Slot<NC>* my = &slots[wave][g];
-        gather_hbm<TV, NC, NG, VEC>(rsrc, my, 0, ni_hbm, lane_off, acc);
-        gather_lds<TV, NC, NG, VEC>(stage, my, ni_hbm, NI, lane_off, acc);
+        gather_hbm<TV, NC, NG, VEC>(rsrc, my, 0, hbm_end, lane_off, acc);
+        gather_lds<TV, NC, NG, VEC>(stage, my, hbm_end, lds_end, lane_off, acc);
 
         const bool store = jb == 0 && c < p.nchunk && q_this + static_cast<uint32_t>(tb) < qb;
         reduce_store<TO, CPL, VEC>(acc, G, store, p.out, row0 + static_cast<uint32_t>(tb * p.M),

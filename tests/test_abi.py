@@ -197,3 +197,21 @@ def test_fused_checks(lib, dims):
     assert fcall(dims, dtype=5) == DTYPE
     assert fcall(dims, S=1 << 31, M=1, D=4) == OVERFLOW
     assert fcall(dims, N=0, ref=0, value=0, out=0, loc=0, attw=0) == OK
+
+
+@pytest.mark.parametrize("dims", [2, 3])
+def test_pruned_checks(lib, dims):
+    def pcall(**kw):
+        a = dict(value=A, dtype=0, shapes=A, starts=A, loc=A, attw=A, thr=0.05, out=A,
+                 out_dtype=0, N=1, S=100, M=8, D=32, Lq=10, L=4, P=4)
+        a.update(kw)
+        return binding.raw_pruned_call(dims, a["value"], a["dtype"], a["shapes"], a["starts"],
+                                       a["loc"], a["attw"], a["thr"], a["out"], a["out_dtype"],
+                                       a["N"], a["S"], a["M"], a["D"], a["Lq"], a["L"], a["P"], 0)
+    for k in ("value", "shapes", "starts", "loc", "attw", "out"):
+        assert pcall(**{k: 0}) == NULL, k
+    assert pcall(out=A + 4) == ALIGN
+    assert pcall(D=3) == UNSUP
+    assert pcall(out_dtype=7) == DTYPE
+    assert pcall(M=1 << 31, D=4) == OVERFLOW
+    assert pcall(N=0, value=0, out=0, loc=0, attw=0) == OK
