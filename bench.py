@@ -51,6 +51,7 @@ COUNTERS_FILES = {
     "forward_fused": os.path.join(ROOT, "profiles", "msda_forward_fused_counters.json"),
     "forward_pruned": os.path.join(ROOT, "profiles", "msda_forward_pruned_counters.json"),
     "backward": os.path.join(ROOT, "profiles", "msda_backward_counters.json"),
+    "linear": os.path.join(ROOT, "profiles", "msda_linear_counters.json"),
 }
 KERNEL_SOURCES = {
     "forward": [os.path.join(CSRC, "msda_device.hpp"), os.path.join(CSRC, "msda_api.hip")],
@@ -58,6 +59,7 @@ KERNEL_SOURCES = {
     "forward_pruned": [os.path.join(CSRC, "msda_device.hpp"), os.path.join(CSRC, "msda_api.hip")],
     "backward": [os.path.join(CSRC, "msda_device.hpp"), os.path.join(CSRC, "msda_backward.hpp"),
                  os.path.join(CSRC, "msda_api.hip")],
+    "linear": [os.path.join(CSRC, "msda_device.hpp"), os.path.join(CSRC, "msda_linear.hip")],
 }
 
 
@@ -184,6 +186,91 @@ def cpu_baseline(w, inp, max_points=60_000_000, grad_out=None, threshold=None):
     }
 
 
+def bench_linear(args):
+    """The value projection W'_m of every pixel of the workload: y[N*S, M*D] =
+    x[N*S, C] W^T + b with C = M*D, as one msda_linear call per step."""
+    import torch
+
+    from scale_deformable_attention_02_amd import msda_linear
+    from scale_deformable_attention_02_amd.workloads import CONFIGS, make_linear_inputs
+
+    w = CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    R, K, N = w.N * w.S, w.M * w.D, w.M * w.D
+    es = 2 if args.linear_dtype == "bf16" else 4
+    flops = 2.0 * R * K * N
+    U = (R * K + N * K + R * N) * es + N * 4
+    copies = max(2, -(-(2 * MALL_BYTES + 1) // U))
+    inp = make_linear_inputs(R, K, N, args.linear_dtype, seed=w.seed)
+    sets = []
+    for c in range(copies):
+        x = inp["x"].to(dev) if c == 0 else sets[0][0].clone()
+        sets.append((x, inp["weight"].to(dev), inp["bias"].to(dev),
+                     torch.empty((R, N), dtype=x.dtype, device=dev)))
+
+    def step(i):
+        x, wt, b, y = sets[i % copies]
+        msda_linear(x, wt, b, out=y)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_s = statistics.mean(a.elapsed_time(b) for a, b in ev) / 1e3
+    peak_tflops = 2500.0 if args.linear_dtype == "bf16" else 157.3
+    t_hbm, t_mfma = U / (HBM_PEAK_GBPS * 1e9), flops / (peak_tflops * 1e12)
+    bound = "hbm" if t_hbm >= t_mfma else "mfma"
+    achieved_gbps, achieved_tflops = U / kernel_s / 1e9, flops / kernel_s / 1e12
+    roof = ({"bound": "hbm", "achieved": achieved_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+             "frac": achieved_gbps / HBM_PEAK_GBPS}
+            if bound == "hbm" else
+            {"bound": "mfma", "achieved": achieved_tflops, "peak": peak_tflops,
+             "unit": "TFLOP/s", "frac": achieved_tflops / peak_tflops})
+    roof["traffic"] = counters_for(w.name, "linear")
+    result = {
+        "metric": "value projection rows/sec + roofline (msda_linear, 1 MI355X)",
+        "value": R / (wall / args.steps),
+        "unit": "rows/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": args.linear_dtype,
+        "data": "synthetic (seeded; no dataset or trained weights)",
+        "config": {"workload": f"{w.name} value projection", "R": R, "K": K, "N": N,
+                   "input_copies_cycled": copies, "parallelism": "single GPU", "op": "linear"},
+        "kernel_us_mean": kernel_s * 1e6,
+        "achieved_hbm_gbps": achieved_gbps,
+        "achieved_tflops": achieved_tflops,
+        "bytes_per_launch": {"compulsory": U},
+        "flops_per_launch": flops,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        import numpy as np
+
+        from oracle import linear_oracle
+        nr = min(R, 20000)
+        t1 = time.perf_counter()
+        linear_oracle(inp["x"][:nr], inp["weight"], inp["bias"])
+        dt = time.perf_counter() - t1
+        result["cpu_baseline"] = {
+            "value": nr / dt, "unit": "rows/s", "cores": int(os.environ.get("OMP_NUM_THREADS", "0")
+                                                            or os.cpu_count() or 1),
+            "kind": "oracle",
+            "sample": f"rows 0..{nr - 1}: fp64 numpy matmul ({np.__version__}) in {dt:.3f} s"}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -191,10 +278,14 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="detr_encoder",
                     help="workload name (default: the DETR encoder configuration)")
-    ap.add_argument("--op", choices=("forward", "forward_fused", "forward_pruned", "backward"),
+    ap.add_argument("--op", choices=("forward", "forward_fused", "forward_pruned", "backward",
+                                     "linear"),
                     default="forward",
                     help="time the forward (default), the forward with the fused front "
-                         "end, the pruned forward, or the backward entry point")
+                         "end, the pruned forward, the backward entry point, or the value "
+                         "projection (msda_linear) of the workload's pixels")
+    ap.add_argument("--linear-dtype", choices=("bf16", "f32"), default="bf16",
+                    help="operand and output dtype of --op linear")
     ap.add_argument("--prune-threshold", type=float, default=None,
                     help="attention-weight threshold of --op forward_pruned "
                          "(default 0.8 / (L*P): about half the samples of softmaxed "
@@ -213,6 +304,9 @@ def main(argv=None):
         return 2
 
     import torch
+
+    if args.op == "linear":
+        return bench_linear(args)
 
     from scale_deformable_attention_02_amd import (msda3d_backward, msda3d_forward,
                                                    msda3d_forward_fused, msda3d_forward_pruned,

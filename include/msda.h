@@ -231,6 +231,26 @@ int msda3d_backward(const void* value, int value_dtype,
                     int64_t N, int64_t S, int64_t M, int64_t D,
                     int64_t Lq, int64_t L, int64_t P, void* stream);
 
+/*
+ * Dense projection on the matrix cores: y = x * weight^T + bias.
+ *   x       [R][K]     x_dtype (MSDA_F32 or MSDA_BF16), 16-byte aligned
+ *   weight  [N][K]     same dtype as x, 16-byte aligned
+ *   bias    float [N]  or NULL (no bias)
+ *   y       [R][N]     y_dtype, 16-byte aligned, overwritten
+ * These are the projections around the core: the value projection W'_m
+ * (R = N_img * S pixels, N = M * D) and the output projection W_m (R = N_img
+ * * Lq queries) of the "Deformable Attention Module" equation, and the linear
+ * layers that predict offsets and attention logits from the query features
+ * ("What is Deformable Attention"; "3D Attention That Knows Where to Look").
+ * Arithmetic: bf16 inputs multiply exactly and accumulate in fp32; fp32
+ * inputs use fp32 matrix FMA; the bias is added in fp32 and the result
+ * rounded once to y_dtype (bf16: nearest even).  K must be a multiple of 32
+ * (MSDA_ERR_UNSUPPORTED); N * K * sizeof(x) < 2^31 (MSDA_ERR_OVERFLOW); R is
+ * split over launches as needed.  R == 0 is a no-op.
+ */
+int msda_linear(const void* x, int x_dtype, const void* weight, const float* bias,
+                void* y, int y_dtype, int64_t R, int64_t K, int64_t N, void* stream);
+
 /* Static, human-readable description of a status code (never NULL). */
 const char* msda_status_string(int status);
 

@@ -17,7 +17,8 @@ sampling locations and attention weights for a given ``grad_out``.
 module's front end: softmax of attention logits (fp64) and location =
 reference point + offset (fp32), then the same forward.
 ``msda_oracle_forward_pruned`` / ``msda3d_oracle_forward_pruned`` drop the
-samples whose attention weight is below a threshold.
+samples whose attention weight is below a threshold.  ``linear_oracle`` is the
+fp64 projection y = x W^T + b.
 """
 from __future__ import annotations
 
@@ -229,3 +230,16 @@ def msda3d_oracle_forward_fused(value, spatial_shapes, level_start_index, refere
     components)."""
     return _run_fused(3, value, spatial_shapes, level_start_index, reference_points,
                       sampling_offsets, attention_logits)
+
+
+def linear_oracle(x, weight, bias=None) -> np.ndarray:
+    """Projection y = x @ weight^T + bias in float64 (inputs widened exactly):
+    the per-pixel linear maps W'_m and W_m of the "Deformable Attention
+    Module" equation and the query-side predictions of offsets and logits.
+    A library matmul serves as the one step; no blocking or reordering."""
+    xd = _as_numpy(x, np.float64)
+    wd = _as_numpy(weight, np.float64)
+    y = xd @ wd.T
+    if bias is not None:
+        y = y + _as_numpy(bias, np.float64)[None, :]
+    return y

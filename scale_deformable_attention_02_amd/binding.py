@@ -2,7 +2,8 @@
 
 ``msda_forward`` / ``msda3d_forward``, ``msda_forward_pruned`` /
 ``msda3d_forward_pruned``, ``msda_forward_fused`` / ``msda3d_forward_fused``
-and ``msda_backward`` / ``msda3d_backward`` take torch tensors that already live on the GPU, check
+and ``msda_backward`` / ``msda3d_backward``, and the projection ``msda_linear``
+take torch tensors that already live on the GPU, check
 dtypes/shapes/contiguity, allocate outputs with torch when the caller passes
 none, and call the same-named C entry point of ``libmsda.so`` on torch's
 current HIP stream.  Every step of the computation
@@ -36,7 +37,7 @@ STATUS = {
 # Every symbol include/msda.h declares.
 EXPORTED = ("msda_forward", "msda3d_forward", "msda_forward_pruned", "msda3d_forward_pruned",
             "msda_forward_fused", "msda3d_forward_fused", "msda_backward", "msda3d_backward",
-            "msda_status_string")
+            "msda_linear", "msda_status_string")
 
 _lib = None
 
@@ -85,6 +86,8 @@ def load_library() -> ctypes.CDLL:
         fn.restype = ctypes.c_int
         fn.argtypes = [vp, ctypes.c_int, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp,
                        i64, i64, i64, i64, i64, i64, i64, vp]
+    lib.msda_linear.restype = ctypes.c_int
+    lib.msda_linear.argtypes = [vp, ctypes.c_int, vp, vp, vp, ctypes.c_int, i64, i64, i64, vp]
     lib.msda_status_string.restype = ctypes.c_char_p
     lib.msda_status_string.argtypes = [ctypes.c_int]
     _lib = lib
@@ -349,3 +352,43 @@ def msda3d_forward_fused(value, spatial_shapes, level_start_index, reference_poi
     """3D counterpart of ``msda_forward_fused`` (3-component points)."""
     return _forward_fused(3, value, spatial_shapes, level_start_index, reference_points,
                           sampling_offsets, attention_logits, out, out_dtype, stream)
+
+
+def raw_linear_call(x_ptr: int, x_dtype: int, w_ptr: int, bias_ptr: int, y_ptr: int,
+                    y_dtype: int, R: int, K: int, N: int, stream: int = 0) -> int:
+    """Call msda_linear with raw pointers; returns the msda_status."""
+    return load_library().msda_linear(x_ptr, x_dtype, w_ptr, bias_ptr, y_ptr, y_dtype,
+                                      R, K, N, stream)
+
+
+def msda_linear(x, weight, bias=None, out=None, out_dtype=None, stream=None) -> torch.Tensor:
+    """Projection ``out = x @ weight.T + bias`` on the matrix cores: x [R, K]
+    and weight [N, K] both float32 or both bfloat16 (contiguous GPU tensors),
+    bias float32 [N] or None; out [R, N] of ``out_dtype`` (default x's).
+    K must be a multiple of 32."""
+    for name, t in (("x", x), ("weight", weight)):
+        if not t.is_cuda or not t.is_contiguous() or t.dim() != 2:
+            raise ValueError(f"{name} must be a contiguous 2-D GPU tensor")
+    if x.dtype != weight.dtype:
+        raise TypeError("x and weight must have the same dtype")
+    code = _dtype_code(x.dtype, "x")
+    R, K = x.shape
+    N, K2 = weight.shape
+    if K2 != K:
+        raise ValueError("weight must be [N, K] with x's K")
+    if bias is not None and (not bias.is_cuda or bias.dtype != torch.float32
+                             or tuple(bias.shape) != (N,) or not bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous float32 [N] GPU tensor")
+    if out is None:
+        out = torch.empty((R, N), dtype=x.dtype if out_dtype is None else out_dtype,
+                          device=x.device)
+    elif tuple(out.shape) != (R, N) or not out.is_contiguous() or out.device != x.device:
+        raise ValueError("out must be a contiguous [R, N] tensor on x's device")
+    ycode = _dtype_code(out.dtype, "out")
+    s = stream if stream is not None else torch.cuda.current_stream(x.device)
+    status = raw_linear_call(x.data_ptr(), code, weight.data_ptr(),
+                             0 if bias is None else bias.data_ptr(), out.data_ptr(), ycode,
+                             R, K, N, s.cuda_stream)
+    if status != 0:
+        raise MsdaError(status, status_string(status))
+    return out

@@ -264,3 +264,20 @@ def make_grad_out(w: Workload, dtype: Optional[str] = None,
     elif dt != "f32":
         raise ValueError(f"unknown grad dtype {dt!r}")
     return grad.contiguous()
+
+
+def make_linear_inputs(R: int, K: int, N: int, dtype: str = "bf16", seed: int = 2024,
+                       bias: bool = True) -> Dict[str, torch.Tensor]:
+    """Seeded operands of a projection y = x W^T + b: x ~ N(0, 1) [R, K],
+    W ~ N(0, 1/K) [N, K] (unit-variance outputs), both rounded to bf16 (RNE)
+    when ``dtype`` is "bf16"; b ~ N(0, 0.02) float32 [N] or None."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    x = torch.randn((R, K), generator=g, dtype=torch.float32)
+    w = torch.randn((N, K), generator=g, dtype=torch.float32) / (K ** 0.5)
+    b = torch.randn((N,), generator=g, dtype=torch.float32) * 0.02 if bias else None
+    if dtype == "bf16":
+        x, w = x.to(torch.bfloat16), w.to(torch.bfloat16)
+    elif dtype != "f32":
+        raise ValueError(f"unknown dtype {dtype!r}")
+    return {"x": x.contiguous(), "weight": w.contiguous(), "bias": b}

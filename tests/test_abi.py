@@ -215,3 +215,19 @@ def test_pruned_checks(lib, dims):
     assert pcall(out_dtype=7) == DTYPE
     assert pcall(M=1 << 31, D=4) == OVERFLOW
     assert pcall(N=0, value=0, out=0, loc=0, attw=0) == OK
+
+
+def test_linear_checks(lib):
+    def lcall(**kw):
+        a = dict(x=A, xd=1, w=A, b=A, y=A, yd=1, R=100, K=256, N=256)
+        a.update(kw)
+        return binding.raw_linear_call(a["x"], a["xd"], a["w"], a["b"], a["y"], a["yd"],
+                                       a["R"], a["K"], a["N"], 0)
+    for k in ("x", "w", "y"):
+        assert lcall(**{k: 0}) == NULL, k
+    assert lcall(R=-1) == DIM and lcall(K=0) == DIM and lcall(N=0) == DIM
+    assert lcall(xd=3) == DTYPE and lcall(yd=-1) == DTYPE
+    assert lcall(K=48) == UNSUP
+    assert lcall(x=A + 8) == ALIGN and lcall(y=A + 2) == ALIGN and lcall(b=A + 2) == ALIGN
+    assert lcall(N=1 << 20, K=1 << 11) == OVERFLOW
+    assert lcall(R=0, x=0, w=0, y=0) == OK
