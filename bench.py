@@ -226,6 +226,14 @@ def bench_linear(args):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kernel_s = statistics.mean(a.elapsed_time(b) for a, b in ev) / 1e3
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     peak_tflops = 2500.0 if args.linear_dtype == "bf16" else 157.3
     t_hbm, t_mfma = U / (HBM_PEAK_GBPS * 1e9), flops / (peak_tflops * 1e12)
     bound = "hbm" if t_hbm >= t_mfma else "mfma"
