@@ -27,7 +27,16 @@
 #define MSDA_STAGED_MIN_TILES 65536
 #endif
 
+// Backward: workgroups of kDedupWaves waves of one (image, head) slice sum
+// the contributions to each grad_value row before the atomics (2D, D <= 64,
+// launches of at least MSDA_DEDUP_MIN_TILES tiles).
+#ifndef MSDA_DEDUP_MIN_TILES
+#define MSDA_DEDUP_MIN_TILES 65536
+#endif
+
 namespace {
+
+constexpr int kDedupWaves = 16;
 
 using msda::FastDiv;
 using msda::Params;
@@ -270,6 +279,14 @@ int forward(const void* value, int value_dtype, const int64_t* spatial_shapes,
 
 template <typename TV, typename TG, int DIM, int CPL>
 void launch_bwd_one(const msda::BwdParams& bp, hipStream_t stream) {
+    if constexpr (DIM == 2) {
+        if (bp.dedup) {
+            hipLaunchKernelGGL((msda::msda_backward_kernel<TV, TG, DIM, CPL, kDedupWaves, true>),
+                               dim3(bp.f.num_blocks), dim3(kDedupWaves * msda::kWave), 0, stream,
+                               bp);
+            return;
+        }
+    }
     hipLaunchKernelGGL((msda::msda_backward_kernel<TV, TG, DIM, CPL>), dim3(bp.f.num_blocks),
                        dim3(msda::kBlockThreads), 0, stream, bp);
 }
@@ -387,10 +404,17 @@ int backward(const void* value, int value_dtype, const int64_t* spatial_shapes,
         const int64_t nbatch = (N - n0 < nb) ? N - n0 : nb;
         for (int64_t q0 = 0; q0 < Lq; q0 += nq) {
             const int64_t nquery = (Lq - q0 < nq) ? Lq - q0 : nq;
-            const int64_t waves_per_slice = (nquery + T - 1) / T;
+            // de-duplication: workgroups of kDedupWaves waves that stay in
+            // one slice (waves per slice padded to a multiple)
+            const bool dedup = DIM == 2 && D <= 64 &&
+                               nbatch * M * nquery >= MSDA_DEDUP_MIN_TILES;
+            const int64_t wave_group = dedup ? kDedupWaves : msda::kWavesPerBlock;
+            int64_t waves_per_slice = (nquery + T - 1) / T;
+            if (dedup) waves_per_slice = (waves_per_slice + wave_group - 1) / wave_group * wave_group;
             const int64_t waves = nbatch * M * waves_per_slice;
             const int64_t first_row = (n0 * Lq + q0) * M;
             msda::BwdParams bp{};
+            bp.dedup = dedup ? 1u : 0u;
             Params& p = bp.f;
             p.value = static_cast<const char*>(value) + n0 * image_bytes;
             p.shapes = spatial_shapes;
@@ -405,8 +429,7 @@ int backward(const void* value, int value_dtype, const int64_t* spatial_shapes,
             p.head_bytes = static_cast<uint32_t>(head_bytes);
             p.out_head_bytes = 0;
             p.image_bytes = static_cast<uint32_t>(image_bytes);
-            p.num_blocks = static_cast<uint32_t>((waves + msda::kWavesPerBlock - 1) /
-                                                 msda::kWavesPerBlock);
+            p.num_blocks = static_cast<uint32_t>((waves + wave_group - 1) / wave_group);
             p.waves = static_cast<uint32_t>(waves);
             p.M = static_cast<int32_t>(M);
             p.Lq = static_cast<int32_t>(Lq);

@@ -25,6 +25,8 @@
 // with 8 dwords per 128-byte row per instruction runs 4x slower.
 #pragma once
 
+#include <type_traits>
+
 #include "msda_device.hpp"
 
 namespace msda {
@@ -40,6 +42,7 @@ struct BwdParams {
     uint32_t gout_head_bytes;    // D * sizeof(grad_out)
     uint32_t value_shift;        // log2(4 / sizeof(value)): grad offset -> value offset
     uint32_t log2R;              // log2 of D rounded up to a power of two
+    uint32_t dedup;              // 1: the de-duplicating workgroups run
 };
 
 // Output-gradient rows of one wave's tiles: T * D floats <= 64 * 16 / sizeof(value)
@@ -146,16 +149,75 @@ __device__ __forceinline__ void load_grad(__amdgpu_buffer_rsrc_t r, uint32_t off
     }
 }
 
-template <typename TV, typename TG, int DIM, int CPL>
-__global__ __launch_bounds__(kBlockThreads) void msda_backward_kernel(BwdParams bp) {
+// Rows of grad_value per workgroup that the de-duplicating variant can
+// collect contributions for (slot tables of 4 B counts and offsets).
+constexpr int kDedupSlots = 4096;
+
+// FastDiv built on the device (the host's construction): exact for x < 2^31.
+__device__ __forceinline__ FastDiv make_fast_div_dev(uint32_t d) {
+    uint32_t l = 0;
+    while ((1ull << l) < d) ++l;
+    const uint64_t shift = 31 + l;
+    const uint64_t mul = ((1ull << shift) + d - 1) / d;
+    return FastDiv{static_cast<uint32_t>(mul), static_cast<uint32_t>(shift)};
+}
+
+struct DedupShared {
+    uint32_t bbox[kMaxLevels][4];   // per level: ~min x, ~min y, max x, max y (max-reduced)
+    int base[kMaxLevels];           // first slot of the level's window, or -1
+    int ox[kMaxLevels], oy[kMaxLevels], ww[kMaxLevels], rows[kMaxLevels];
+    FastDiv div_ww[kMaxLevels];
+    int nslots;
+    int any_direct;                 // some level takes the direct atomics of phase C
+    uint32_t wave_sum[16];
+    uint32_t count[kDedupSlots];
+    uint32_t offs[kDedupSlots + 1];
+};
+
+struct DedupEntry {
+    float aw;      // A * w_c
+    uint32_t gi;   // float offset of the sample's output-gradient row in the workgroup's tile
+};
+
+// Integer cell of a sample (same arithmetic as make_bwd_slot): whether it
+// touches the level, and floor of its pixel-space coordinates.
+template <int DIM>
+__device__ __forceinline__ bool bwd_cell(const float (&xyz)[DIM], bool live, const LevelGeom& lg,
+                                         int& x0, int& y0) {
+    const float Wf = static_cast<float>(lg.W), Hf = static_cast<float>(lg.H);
+    const float xh = fmaf(xyz[0], Wf, -0.5f);
+    const float yh = fmaf(xyz[1], Hf, -0.5f);
+    bool inside = live && xh > -1.0f && xh < Wf && yh > -1.0f && yh < Hf;
+    if constexpr (DIM == 3) {
+        const float Zf = static_cast<float>(lg.Z);
+        const float zh = fmaf(xyz[2], Zf, -0.5f);
+        inside = inside && zh > -1.0f && zh < Zf;
+    }
+    x0 = inside ? static_cast<int>(floorf(xh)) : 0;
+    y0 = inside ? static_cast<int>(floorf(yh)) : 0;
+    return inside;
+}
+
+// WAVES waves per workgroup.  DEDUP (2D, D <= 64, WAVES consecutive waves of
+// one (image, head) slice): contributions to grad_value rows that several
+// samples of the workgroup touch are summed in registers before one atomic
+// row update (see phase D).
+template <typename TV, typename TG, int DIM, int CPL, int WAVES = kWavesPerBlock,
+          bool DEDUP = false>
+__global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams bp) {
     constexpr int NC = DIM == 2 ? 4 : 8;
     constexpr int NG = kWave / CPL;
     constexpr int VEC = ValueTraits<TV>::kVec;
+    constexpr int kThreads = WAVES * kWave;
+    static_assert(!DEDUP || (DIM == 2 && 4 * kThreads >= kDedupSlots),
+                  "de-duplication: 2D, four table slots per thread at most");
     const Params& p = bp.f;
 
     __shared__ LevelGeom smeta[kMaxSamplesPerTile];
-    __shared__ BwdSlot<NC, DIM> slots[kWavesPerBlock][kWave];
-    __shared__ float gtile[kWavesPerBlock][kGradTileFloats];
+    __shared__ BwdSlot<NC, DIM> slots[WAVES][kWave];
+    __shared__ float gtile[WAVES][kGradTileFloats];
+    using DedupT = typename std::conditional<DEDUP, DedupShared, int>::type;
+    __shared__ DedupT dd;
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -171,9 +233,14 @@ __global__ __launch_bounds__(kBlockThreads) void msda_backward_kernel(BwdParams 
         smeta[tid] = level_geom<DIM>(p.shapes, p.starts, l, grow_bytes);
     }
 
+    if constexpr (DEDUP) {
+        for (int i = tid; i < kDedupSlots; i += kThreads) dd.count[i] = 0u;
+        if (tid < kMaxLevels * 4) (&dd.bbox[0][0])[tid] = 0u;   // ~min = 0 means +inf
+    }
+
     const uint32_t blk = xcd_contiguous_block(blockIdx.x, p.num_blocks);
     const uint32_t wave_id =
-        __builtin_amdgcn_readfirstlane(blk * kWavesPerBlock + static_cast<uint32_t>(wave));
+        __builtin_amdgcn_readfirstlane(blk * WAVES + static_cast<uint32_t>(wave));
     const bool wave_live = wave_id < p.waves;
     const uint32_t slice = fast_div(wave_id, p.div_wps);
     const uint32_t q0 = (wave_id - slice * p.wps) * static_cast<uint32_t>(p.T);
@@ -184,6 +251,9 @@ __global__ __launch_bounds__(kBlockThreads) void msda_backward_kernel(BwdParams 
     const int G = 1 << p.log2G;
 
     // ---- Phase A: lane k fills slot k = i*NG + g.
+    BwdSlot<NC, DIM> mine;           // this lane's sample (kept for phase D)
+    int my_level = 0, my_x0 = 0, my_y0 = 0, my_tile = 0;
+    bool my_in = false;
     {
         const int i = lane / NG, g = lane % NG;
         const int t = g >> p.log2G, j = g & (G - 1);
@@ -198,8 +268,13 @@ __global__ __launch_bounds__(kBlockThreads) void msda_backward_kernel(BwdParams 
         load_sample<DIM>(p, live, sidx, xyz, a);
         __syncthreads();  // smeta is ready
         const LevelGeom lg = smeta[s_c];
-        slots[wave][lane] =
-            make_bwd_slot<DIM>(xyz, a, live, sidx, lg, ghead_base + lg.start_bytes, grow_bytes);
+        mine = make_bwd_slot<DIM>(xyz, a, live, sidx, lg, ghead_base + lg.start_bytes, grow_bytes);
+        slots[wave][lane] = mine;
+        if constexpr (DEDUP) {
+            my_level = static_cast<int>(fast_div(static_cast<uint32_t>(s_c), p.div_P));
+            my_in = bwd_cell<DIM>(xyz, live, lg, my_x0, my_y0) && mine.a != 0.0f;
+            my_tile = wave * kGradTileFloats + t * p.nchunk * VEC;
+        }
     }
     __syncthreads();
 
@@ -292,15 +367,79 @@ __global__ __launch_bounds__(kBlockThreads) void msda_backward_kernel(BwdParams 
         }
     }
 
+    // ---- Phase D1 (de-duplication): each level's window is the bounding box
+    // of the pixels its samples' cells cover in this workgroup; levels whose
+    // windows fit kDedupSlots (smallest first) collect their contributions
+    // per pixel row.  Other levels keep the direct atomics of phase C.
+    if constexpr (DEDUP) {
+        for (int l = 0; l < p.L; ++l) {
+            uint32_t v[4];
+            const bool mine_l = my_in && my_level == l;
+            v[0] = mine_l ? ~static_cast<uint32_t>(max(my_x0, 0)) : 0u;
+            v[1] = mine_l ? ~static_cast<uint32_t>(max(my_y0, 0)) : 0u;
+            v[2] = mine_l ? static_cast<uint32_t>(min(my_x0 + 1, smeta[l * p.P].W - 1)) : 0u;
+            v[3] = mine_l ? static_cast<uint32_t>(min(my_y0 + 1, smeta[l * p.P].H - 1)) : 0u;
+#pragma unroll
+            for (int b = 1; b < kWave; b <<= 1)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    v[e] = max(v[e], static_cast<uint32_t>(__shfl_xor(static_cast<int>(v[e]), b, kWave)));
+            if (lane == 0 && v[0] != 0u) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) atomicMax(&dd.bbox[l][e], v[e]);
+            }
+        }
+        __syncthreads();
+        if (tid < p.L) {
+            const uint32_t lo_x = ~dd.bbox[tid][0], lo_y = ~dd.bbox[tid][1];
+            const uint32_t hi_x = dd.bbox[tid][2], hi_y = dd.bbox[tid][3];
+            const bool any = dd.bbox[tid][0] != 0u;
+            const int w = any ? static_cast<int>(hi_x - lo_x) + 1 : 0;
+            const int h = any ? static_cast<int>(hi_y - lo_y) + 1 : 0;
+            dd.ox[tid] = static_cast<int>(lo_x);
+            dd.oy[tid] = static_cast<int>(lo_y);
+            dd.ww[tid] = w > 0 ? w : 1;
+            dd.rows[tid] = w * h;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            // windows in ascending size (ties by level) while the total fits
+            // the table; the total only grows, so a level that does not fit
+            // excludes every larger one
+            int nslots = 0;
+            for (int l = 0; l < p.L; ++l) {
+                const int mine_rows = dd.rows[l];
+                int before = 0;
+                for (int k = 0; k < p.L; ++k) {
+                    const int r = dd.rows[k];
+                    if (r < mine_rows || (r == mine_rows && k < l)) before += r;
+                }
+                const bool fits = mine_rows > 0 && before + mine_rows <= kDedupSlots;
+                dd.base[l] = fits ? before : -1;
+                dd.div_ww[l] = make_fast_div_dev(static_cast<uint32_t>(dd.ww[l]));
+                if (fits) nslots = max(nslots, before + mine_rows);
+            }
+            dd.nslots = nslots;
+            int any = 0;
+            for (int l = 0; l < p.L; ++l) any |= dd.base[l] < 0 && dd.rows[l] > 0 ? 1 : 0;
+            dd.any_direct = any;
+        }
+        __syncthreads();
+    }
+
     // ---- Phase C: grad_value[row_c][d] += A * w_c * g[t][d] over the flat
     // index (slot, corner, channel padded to R); 64 / R rows per instruction
     // (R <= 64), or a row in R / 64 instructions.  NG * R >= 128, so the trip
-    // count is the same on every lane.
+    // count is the same on every lane.  With DEDUP only levels without a
+    // window take this path.
     wave_lds_sync();
     constexpr int kLog2NC = DIM == 2 ? 2 : 3;
     const uint32_t log2R = bp.log2R;
     const uint32_t rmask = (1u << log2R) - 1u;
-    const uint32_t total = static_cast<uint32_t>(p.NI * NG) << (log2R + kLog2NC);
+    uint32_t total = static_cast<uint32_t>(p.NI * NG) << (log2R + kLog2NC);
+    if constexpr (DEDUP) {
+        if (!dd.any_direct) total = 0u;   // every contribution goes through phase D
+    }
     const int log2G = p.log2G;
     for (uint32_t f = static_cast<uint32_t>(lane); f < total; f += kWave) {
         const uint32_t d = f & rmask;
@@ -309,11 +448,114 @@ __global__ __launch_bounds__(kBlockThreads) void msda_backward_kernel(BwdParams 
         const BwdSlot<NC, DIM>* sp = &slots[wave][sig];
         const uint32_t off = sp->off[k];
         const float a = sp->a;
-        if (d < static_cast<uint32_t>(D) && off != kOutOfRange && a != 0.0f) {
+        bool direct = true;
+        if constexpr (DEDUP) {
+            const int gs = static_cast<int>(sig & (NG - 1));
+            const int ss = static_cast<int>(sig / NG) * G + (gs & (G - 1));
+            const int ls = static_cast<int>(fast_div(static_cast<uint32_t>(min(ss, p.LP - 1)), p.div_P));
+            direct = dd.base[ls] < 0;
+        }
+        if (direct && d < static_cast<uint32_t>(D) && off != kOutOfRange && a != 0.0f) {
             const int ts = static_cast<int>(sig & (NG - 1)) >> log2G;
             const float gd = gtile[wave][ts * D + static_cast<int>(d)];
             __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(a * sp->w[k] * gd, rgv, off + 4u * d,
                                                             0, 0);
+        }
+    }
+
+    // ---- Phase D (de-duplication).  D2: each contribution of a windowed
+    // level takes a place in its pixel's list (LDS integer atomics); D3:
+    // exclusive prefix sum of the counts; D4: entries (A*w, tile row) are
+    // written to the lists, over the slot array, which is no longer read;
+    // D5: groups of R lanes sum each pixel's list, channel per lane, and add
+    // the row to grad_value with one coalesced atomic per channel.
+    if constexpr (DEDUP) {
+        uint32_t slot_id[NC], pos[NC];
+#pragma unroll
+        for (int k = 0; k < NC; ++k) {
+            slot_id[k] = 0xffffffffu;
+            pos[k] = 0u;
+            const int cx = k & 1, cy = (k >> 1) & 1;
+            const int base = dd.base[my_level];
+            if (my_in && base >= 0 && mine.off[k] != kOutOfRange) {
+                const int x = my_x0 + cx - dd.ox[my_level];
+                const int y = my_y0 + cy - dd.oy[my_level];
+                slot_id[k] = static_cast<uint32_t>(base + y * dd.ww[my_level] + x);
+                pos[k] = atomicAdd(&dd.count[slot_id[k]], 1u);
+            }
+        }
+        __syncthreads();
+        // D3: exclusive scan of count[0, nslots) into offs (4 slots per thread)
+        const int nslots = dd.nslots;
+        {
+            const int i0 = 4 * tid;
+            uint32_t cv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) cv[e] = i0 + e < nslots ? dd.count[i0 + e] : 0u;
+            const uint32_t mine_sum = cv[0] + cv[1] + cv[2] + cv[3];
+            uint32_t incl = mine_sum;
+#pragma unroll
+            for (int b = 1; b < kWave; b <<= 1) {
+                const uint32_t o = static_cast<uint32_t>(__shfl_up(static_cast<int>(incl), b, kWave));
+                if (lane >= b) incl += o;
+            }
+            if (lane == kWave - 1) dd.wave_sum[wave] = incl;
+            __syncthreads();
+            uint32_t before = 0u;
+            for (int w = 0; w < wave; ++w) before += dd.wave_sum[w];
+            uint32_t run = before + incl - mine_sum;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if (i0 + e < nslots) dd.offs[i0 + e] = run;
+                run += cv[e];
+            }
+            if (tid == kThreads - 1) {
+                uint32_t all = 0u;
+                for (int w = 0; w < WAVES; ++w) all += dd.wave_sum[w];
+                dd.offs[nslots] = all;
+            }
+        }
+        __syncthreads();
+        DedupEntry* list = reinterpret_cast<DedupEntry*>(&slots[0][0]);
+#pragma unroll
+        for (int k = 0; k < NC; ++k) {
+            if (slot_id[k] != 0xffffffffu) {
+                DedupEntry e;
+                e.aw = mine.a * mine.w[k];
+                e.gi = static_cast<uint32_t>(my_tile);   // gtile float offset of the row
+                list[dd.offs[slot_id[k]] + pos[k]] = e;
+            }
+        }
+        __syncthreads();
+        // D5: level by level, groups of R lanes take every ngroups-th pixel
+        const int rl = 1 << log2R;               // lanes per row (D <= 64)
+        const int ngroups = kThreads / rl;
+        const int grp = tid / rl, ch = tid % rl;
+        const float* gflat = &gtile[0][0];
+        for (int l = 0; l < p.L; ++l) {
+            const int base = dd.base[l];
+            if (base < 0) continue;
+            const int rows = dd.rows[l];
+            const int ww = dd.ww[l], ox = dd.ox[l], oy = dd.oy[l];
+            const FastDiv dw = dd.div_ww[l];
+            const LevelGeom lg = smeta[l * p.P];
+            for (int local = grp; local < rows; local += ngroups) {
+                const uint32_t b0 = dd.offs[base + local], b1 = dd.offs[base + local + 1];
+                if (b0 == b1) continue;
+                float acc = 0.0f;
+                for (uint32_t e = b0; e < b1; ++e) {
+                    const DedupEntry en = list[e];
+                    acc = fmaf(en.aw, ch < D ? gflat[en.gi + static_cast<uint32_t>(ch)] : 0.0f, acc);
+                }
+                const uint32_t y = fast_div(static_cast<uint32_t>(local), dw);
+                const uint32_t x = static_cast<uint32_t>(local) - y * static_cast<uint32_t>(ww);
+                const uint32_t pix = (static_cast<uint32_t>(oy) + y) * static_cast<uint32_t>(lg.W) +
+                                     static_cast<uint32_t>(ox) + x;
+                const uint32_t off = ghead_base + lg.start_bytes + pix * grow_bytes;
+                if (ch < D)
+                    __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(
+                        acc, rgv, off + 4u * static_cast<uint32_t>(ch), 0, 0);
+            }
         }
     }
 }
