@@ -8,21 +8,27 @@
 // a linear projection of the query; "3D Attention That Knows Where to Look":
 // weights from a small linear layer).
 //
-// Kernel: a 256-thread workgroup computes a 128 x 128 tile of Y; its 4 waves
-// each own 64 x 64 = 2 x 2 MFMA tiles of 32 x 32 with fp32 accumulators.  K
-// advances in steps of 32: each step's X and W tiles are copied global ->
-// registers -> LDS (double buffered, the next step's global loads in flight
-// while the current one is multiplied).  bf16 operands use
-// v_mfma_f32_32x32x16_bf16 (lane l: row l%32, 8 consecutive k at 8*(l/32)),
-// fp32 operands v_mfma_f32_32x32x2_f32 (lane l: row l%32, k = l/32) with the
-// k order inside a step permuted so each lane reads 16 consecutive floats.
-// The result of lane l, element j is row 8*(j/4) + 4*(l/32) + j%4, column
-// l%32.  Epilogue: + bias, round to the output type (bf16: RNE), store.
+// Kernels: a 256-thread workgroup computes a 128 x 128 tile of Y; its 4
+// waves each own 64 x 64 = 2 x 2 MFMA tiles of 32 x 32 with fp32
+// accumulators, which start at the bias (so the bias is the first term of
+// each sum).  K advances in steps of 32.  bf16 operands: the X and W tiles of
+// each step go straight from global memory into LDS (global_load_lds, no
+// registers), several steps in flight; v_mfma_f32_32x32x16_bf16 (lane l: row
+// l%32, 8 consecutive k at 8*(l/32)).  fp32 operands: each step's tiles are
+// copied global -> registers -> LDS, double buffered;
+// v_mfma_f32_32x32x2_f32 (lane l: row l%32, k = l/32) with the k order inside
+// a step permuted so each lane reads 16 consecutive floats.  The W rows are
+// the MFMA's first operand, so a tile holds Y transposed: lane l, element j
+// is column 8*(j/4) + 4*(l/32) + j%4 of row l%32, four consecutive columns
+// per lane.  Epilogue: round to the output type (bf16: RNE) and store four
+// (or, bf16, eight) consecutive columns at a time.
 #include "msda.h"
 
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "msda_device.hpp"
 
@@ -30,6 +36,8 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
 
 constexpr int kBM = 128, kBN = 128, kBK = 32;
 constexpr int kThreads = 256;
@@ -44,7 +52,7 @@ struct LinearParams {
     const void* w;
     const float* bias;     // may be null
     void* y;               // this launch's rows
-    uint32_t x_bytes, w_bytes;
+    uint32_t x_bytes, w_bytes, y_bytes;
     int32_t R, K, N;       // rows in this launch, reduction, output columns
     uint32_t tiles_n;      // ceil(N / kBN)
     uint32_t num_blocks;
@@ -131,7 +139,7 @@ __device__ __forceinline__ void mma_step(const unsigned char* la, const unsigned
             for (int i = 0; i < 2; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
         }
     } else {
         // lane half h takes k = 16 h + kk of the step: 16 consecutive floats
@@ -154,25 +162,270 @@ __device__ __forceinline__ void mma_step(const unsigned char* la, const unsigned
                     for (int j = 0; j < 2; ++j) {
                         const float av = e == 0 ? a[i][v].x : e == 1 ? a[i][v].y : e == 2 ? a[i][v].z : a[i][v].w;
                         const float bv = e == 0 ? b[j][v].x : e == 1 ? b[j][v].y : e == 2 ? b[j][v].z : b[j][v].w;
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc[i][j], 0, 0, 0);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(bv, av, acc[i][j], 0, 0, 0);
                     }
     }
 }
 
 template <typename TY>
-__device__ __forceinline__ void store_y(void* y, uint32_t idx, float v);
+__device__ __forceinline__ void store_y(__amdgpu_buffer_rsrc_t ry, uint32_t byte_off, float v);
 
 template <>
-__device__ __forceinline__ void store_y<float>(void* y, uint32_t idx, float v) {
-    static_cast<float*>(y)[idx] = v;
+__device__ __forceinline__ void store_y<float>(__amdgpu_buffer_rsrc_t ry, uint32_t byte_off, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), ry, byte_off, 0, 0);
+}
+
+// round to nearest even (finite values; NaN stays NaN)
+__device__ __forceinline__ uint32_t bf16_bits(float v) {
+    const uint32_t u = __float_as_uint(v);
+    const uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    return (u & 0x7fffffffu) > 0x7f800000u ? (u >> 16) | 0x40u : r;
 }
 
 template <>
-__device__ __forceinline__ void store_y<msda::Bf16>(void* y, uint32_t idx, float v) {
-    // round to nearest even (finite values; NaN stays NaN)
-    const uint32_t u = __float_as_uint(v);
-    const uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-    static_cast<uint16_t*>(y)[idx] = static_cast<uint16_t>((u & 0x7fffffffu) > 0x7f800000u ? (u >> 16) | 0x40u : r);
+__device__ __forceinline__ void store_y<msda::Bf16>(__amdgpu_buffer_rsrc_t ry, uint32_t byte_off, float v) {
+    __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(bf16_bits(v)), ry, byte_off, 0, 0);
+}
+
+// Four consecutive columns of one row (byte_off aligned to 4 elements).
+template <typename TY>
+__device__ __forceinline__ void store_y4(__amdgpu_buffer_rsrc_t ry, uint32_t byte_off, const float (&v)[4]);
+
+template <>
+__device__ __forceinline__ void store_y4<float>(__amdgpu_buffer_rsrc_t ry, uint32_t byte_off, const float (&v)[4]) {
+    __builtin_amdgcn_raw_buffer_store_b128(
+        v4u{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])},
+        ry, byte_off, 0, 0);
+}
+
+template <>
+__device__ __forceinline__ void store_y4<msda::Bf16>(__amdgpu_buffer_rsrc_t ry, uint32_t byte_off, const float (&v)[4]) {
+    __builtin_amdgcn_raw_buffer_store_b64(
+        v2u{bf16_bits(v[0]) | (bf16_bits(v[1]) << 16), bf16_bits(v[2]) | (bf16_bits(v[3]) << 16)},
+        ry, byte_off, 0, 0);
+}
+
+// Epilogue of a wave's 2 x 2 tiles: round, store.  The MFMAs take the
+// W rows as their first operand, so each tile holds Y transposed: lane l has
+// row l % 32, and its elements 4 g .. 4 g + 3 are the four consecutive
+// columns 8 g + 4 (l / 32) + 0..3.  VEC (the widest that N's alignment
+// allows): 8 = bf16 output with N % 8 == 0, where one v_permlane32_swap per
+// register pair hands lanes 0-31 columns 16 q + 0..7 and lanes 32-63 columns
+// 16 q + 8..15 of their row, stored as 16 B; 4 = one 8 B (bf16) or 16 B (fp32)
+// store per group of four; 1 = element by element.  Rows and columns past the
+// matrix get an out-of-range offset, which the buffer store drops, so the
+// stores issue back to back with no branches.
+template <typename TY, int VEC>
+__device__ __forceinline__ void store_tiles_as(const LinearParams& p, uint32_t row0, uint32_t col0,
+                                               int am, int bn, int lane, const f32x16_t (&acc)[2][2]) {
+    const __amdgpu_buffer_rsrc_t ry = msda::buffer_of(p.y, p.y_bytes);
+    const int r = lane & 31, h = lane >> 5;
+    const uint32_t R = static_cast<uint32_t>(p.R), N = static_cast<uint32_t>(p.N);
+    constexpr uint32_t es = static_cast<uint32_t>(sizeof(TY));
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const uint32_t row = row0 + static_cast<uint32_t>(am + 32 * i + r);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            if constexpr (VEC == 8) {
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    // groups g = 2q (lo) and 2q + 1 (hi), packed to bf16 pairs
+                    uint32_t lo[2], hi[2];
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+                        lo[t] = bf16_bits(acc[i][j][8 * q + 2 * t]) | (bf16_bits(acc[i][j][8 * q + 2 * t + 1]) << 16);
+                        hi[t] = bf16_bits(acc[i][j][8 * q + 4 + 2 * t]) | (bf16_bits(acc[i][j][8 * q + 5 + 2 * t]) << 16);
+                        // lanes 32-63 of lo trade places with lanes 0-31 of hi
+                        const auto sw = __builtin_amdgcn_permlane32_swap(lo[t], hi[t], false, false);
+                        lo[t] = sw[0];
+                        hi[t] = sw[1];
+                    }
+                    const uint32_t col = col0 + static_cast<uint32_t>(bn + 32 * j + 16 * q + 8 * h);
+                    const uint32_t off = (row < R && col < N) ? (row * N + col) * es : msda::kOutOfRange;
+                    __builtin_amdgcn_raw_buffer_store_b128(v4u{lo[0], lo[1], hi[0], hi[1]}, ry, off, 0, 0);
+                }
+            } else {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const uint32_t col = col0 + static_cast<uint32_t>(bn + 32 * j + 8 * g + 4 * h);
+                    float v[4];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) v[t] = acc[i][j][4 * g + t];
+                    if constexpr (VEC == 4) {
+                        const uint32_t off = (row < R && col < N) ? (row * N + col) * es : msda::kOutOfRange;
+                        store_y4<TY>(ry, off, v);
+                    } else {
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) {
+                            const uint32_t off = (row < R && col + t < N) ? (row * N + col + t) * es
+                                                                          : msda::kOutOfRange;
+                            store_y<TY>(ry, off, v[t]);
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
+// The accumulators start at the bias: element e of tile (i, j) is column
+// col0 + bn + 32 j + 8 (e / 4) + 4 (l / 32) + e % 4 (any row).  Columns past
+// N, and a null bias, read as zeros through the buffer's range check.
+__device__ __forceinline__ void init_with_bias(const LinearParams& p, uint32_t col0, int bn, int lane,
+                                               f32x16_t (&acc)[2][2]) {
+    const __amdgpu_buffer_rsrc_t rb = msda::buffer_of(p.bias, p.bias ? static_cast<uint32_t>(p.N) * 4u : 0u);
+    const uint32_t N = static_cast<uint32_t>(p.N);
+    const int h = lane >> 5;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        f32x16_t v;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const uint32_t col = col0 + static_cast<uint32_t>(bn + 32 * j + 8 * (e >> 2) + 4 * h + (e & 3));
+            v[e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, col < N ? col * 4u : msda::kOutOfRange, 0, 0));
+        }
+        acc[0][j] = v;
+        acc[1][j] = v;
+    }
+}
+
+template <typename TY>
+__device__ __forceinline__ void store_tiles(const LinearParams& p, uint32_t row0, uint32_t col0,
+                                            int am, int bn, int lane, const f32x16_t (&acc)[2][2]) {
+    if (std::is_same<TY, msda::Bf16>::value && (p.N & 7) == 0)
+        store_tiles_as<TY, 8>(p, row0, col0, am, bn, lane, acc);
+    else if ((p.N & 3) == 0)
+        store_tiles_as<TY, 4>(p, row0, col0, am, bn, lane, acc);
+    else
+        store_tiles_as<TY, 1>(p, row0, col0, am, bn, lane, acc);
+}
+
+// ---------------------------------------------------------------------------
+// bf16 kernel with a pipeline of direct global -> LDS loads, ST stages of a
+// K step of KB values.  A step of the X and W tiles is 128 rows x 2 KB bytes
+// (CPR = KB / 8 chunks of 16 B per row), stored unpadded with chunk c of row
+// r at position c ^ swz(r), which keeps the b128 operand reads of 8
+// consecutive rows on distinct banks.  A wave's global_load_lds_dwordx4
+// writes 64 consecutive 16 B chunks (lane l at pointer + 16 l), so lane l of
+// load j loads the global chunk that belongs at that position.  Rows past
+// the matrix load a clamped valid row; their results are never stored.
+// ---------------------------------------------------------------------------
+// Measured on the DETR encoder's value projection (R = 44446, K = N = 256):
+// 3 stages of 32 (48 KB LDS, 3 workgroups per CU) beat 4 stages (2 per CU)
+// and K steps of 64 or 128 (fewer workgroups per CU).
+constexpr int kBf16Stages = 3;
+constexpr int kBf16Step = 32;
+
+template <int CPR>
+__device__ __forceinline__ int swz(int r) {
+    static_assert(CPR == 4 || CPR == 8 || CPR == 16, "chunks per row");
+    if constexpr (CPR == 4) return (r >> 1) & 3;
+    else return r & 7;
+}
+
+// Wait until at most N vector-memory instructions of this wave are in flight
+// (lgkm and exp counters not waited on).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Wait for all but the last `after` stages (LOADS instructions each).
+template <int LOADS, int MAXAFTER>
+__device__ __forceinline__ void wait_stages(int after) {
+    if constexpr (MAXAFTER >= 2) {
+        if (after >= 2) { wait_vm<2 * LOADS>(); return; }
+    }
+    if constexpr (MAXAFTER >= 1) {
+        if (after == 1) { wait_vm<LOADS>(); return; }
+    }
+    wait_vm<0>();
+}
+
+template <int KB>
+__device__ __forceinline__ void issue_stage(const uint16_t* base, uint32_t row0, uint32_t rows_valid,
+                                           uint32_t K, uint32_t k0, unsigned char* lds_tile,
+                                           int wave, int lane) {
+    constexpr int CPR = KB / 8, PER_WAVE = 128 * CPR / (4 * msda::kWave);
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+        const int pos = (wave * PER_WAVE + i) * msda::kWave + lane;   // 16 B chunk position in the tile
+        const int r = pos / CPR, cs = pos % CPR;
+        const int c = cs ^ swz<CPR>(r);
+        const uint32_t rr = static_cast<uint32_t>(r) < rows_valid ? static_cast<uint32_t>(r)
+                                                                  : rows_valid - 1u;
+        const uint16_t* src = base + static_cast<size_t>(row0 + rr) * K + k0 + static_cast<uint32_t>(c) * 8u;
+        __builtin_amdgcn_global_load_lds(src, lds_tile + (wave * PER_WAVE + i) * msda::kWave * 16, 16, 0, 0);
+    }
+}
+
+template <typename TY, int KB, int ST>
+__global__ __launch_bounds__(kThreads) void linear_bf16_kernel(LinearParams p) {
+    constexpr int CPR = KB / 8, ROWB = KB * 2, STAGE = 128 * ROWB;
+    constexpr int LOADS = 2 * 128 * CPR / (4 * msda::kWave);   // per wave per stage, X and W
+    static_assert(ST >= 2 && ST <= 4, "the waits count at most two later stages");
+    __shared__ __align__(16) unsigned char lds[ST][2][STAGE];   // [stage][X, W]
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint32_t blk = msda::xcd_contiguous_block(blockIdx.x, p.num_blocks);
+    const uint32_t tm = blk / p.tiles_n, tn = blk - tm * p.tiles_n;
+    const uint32_t row0 = tm * kBM, col0 = tn * kBN;
+    const uint32_t rows_x = min(static_cast<uint32_t>(p.R) - row0, static_cast<uint32_t>(kBM));
+    const uint32_t rows_w = min(static_cast<uint32_t>(p.N) - col0, static_cast<uint32_t>(kBN));
+    const uint16_t* xb = static_cast<const uint16_t*>(p.x);
+    const uint16_t* wb = static_cast<const uint16_t*>(p.w);
+    const uint32_t K = static_cast<uint32_t>(p.K);
+    const int steps = p.K / KB;
+
+    const int am = (wave >> 1) * 64, bn = (wave & 1) * 64;
+    const int r = lane & 31, h = lane >> 5;
+    f32x16_t acc[2][2];
+    init_with_bias(p, col0, bn, lane, acc);
+
+    // prologue: stages 0 .. ST-2
+#pragma unroll
+    for (int st = 0; st < ST - 1; ++st) {
+        if (st < steps) {
+            issue_stage<KB>(xb, row0, rows_x, K, st * KB, lds[st][0], wave, lane);
+            issue_stage<KB>(wb, col0, rows_w, K, st * KB, lds[st][1], wave, lane);
+        }
+    }
+    for (int s = 0; s < steps; ++s) {
+        // stage s has landed once only the stages issued after it are in flight
+        wait_stages<LOADS, ST - 2>(min(s + ST - 2, steps - 1) - s);
+        // every wave's part of stage s is in LDS and stage s-1 is consumed;
+        // a bare barrier: the fence of __syncthreads() would wait for every
+        // load in flight, the later stages included
+        __builtin_amdgcn_s_barrier();
+        __asm__ volatile("" ::: "memory");   // no LDS access moves above the wait and barrier
+        if (s + ST - 1 < steps) {
+            const int st = (s + ST - 1) % ST;
+            issue_stage<KB>(xb, row0, rows_x, K, (s + ST - 1) * KB, lds[st][0], wave, lane);
+            issue_stage<KB>(wb, col0, rows_w, K, (s + ST - 1) * KB, lds[st][1], wave, lane);
+        }
+        const unsigned char* la = lds[s % ST][0];
+        const unsigned char* lb = lds[s % ST][1];
+#pragma unroll
+        for (int kk = 0; kk < KB / 16; ++kk) {
+            const int c = kk * 2 + h;
+            bf16x8_t a[2], b[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int ra = am + 32 * t + r, rb = bn + 32 * t + r;
+                a[t] = *reinterpret_cast<const bf16x8_t*>(la + ra * ROWB + ((c ^ swz<CPR>(ra)) << 4));
+                b[t] = *reinterpret_cast<const bf16x8_t*>(lb + rb * ROWB + ((c ^ swz<CPR>(rb)) << 4));
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+        }
+    }
+
+    store_tiles<TY>(p, row0, col0, am, bn, lane, acc);
 }
 
 template <typename TX, typename TY>
@@ -195,10 +448,7 @@ __global__ __launch_bounds__(kThreads) void linear_kernel(LinearParams p) {
 
     const int am = (wave >> 1) * 64, bn = (wave & 1) * 64;
     f32x16_t acc[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
+    init_with_bias(p, col0, bn, lane, acc);
 
     uint32_t bx[Tile<TX>::kChunks][4], bw[Tile<TX>::kChunks][4];
     Tile<TX>::load(rx, row0, rows_x, 0, K, tid, bx);
@@ -223,28 +473,17 @@ __global__ __launch_bounds__(kThreads) void linear_kernel(LinearParams p) {
         __syncthreads();
     }
 
-    // epilogue: + bias, round, store (lanes 0-31 / 32-63 write consecutive columns)
-    const int c = lane & 31, h = lane >> 5;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const uint32_t col = col0 + static_cast<uint32_t>(bn + 32 * j + c);
-        const bool col_ok = col < static_cast<uint32_t>(p.N);
-        const float b = (p.bias && col_ok) ? p.bias[col] : 0.0f;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const uint32_t row = row0 + static_cast<uint32_t>(am + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3));
-                if (col_ok && row < static_cast<uint32_t>(p.R))
-                    store_y<TY>(p.y, row * static_cast<uint32_t>(p.N) + col, acc[i][j][e] + b);
-            }
-        }
-    }
+    store_tiles<TY>(p, row0, col0, am, bn, lane, acc);
 }
 
 template <typename TX, typename TY>
 void launch_linear(const LinearParams& p, hipStream_t s) {
-    hipLaunchKernelGGL((linear_kernel<TX, TY>), dim3(p.num_blocks), dim3(kThreads), 0, s, p);
+    static_assert(kBf16Step == kBK, "K is checked against kBK");
+    if constexpr (std::is_same<TX, msda::Bf16>::value)
+        hipLaunchKernelGGL((linear_bf16_kernel<TY, kBf16Step, kBf16Stages>), dim3(p.num_blocks),
+                           dim3(kThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL((linear_kernel<TX, TY>), dim3(p.num_blocks), dim3(kThreads), 0, s, p);
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -282,6 +521,7 @@ extern "C" int msda_linear(const void* x, int x_dtype, const void* weight, const
         p.y = static_cast<char*>(y) + r0 * N * ye;
         p.x_bytes = static_cast<uint32_t>(nr * K * xe);
         p.w_bytes = static_cast<uint32_t>(N * K * xe);
+        p.y_bytes = static_cast<uint32_t>(nr * N * ye);
         p.R = static_cast<int32_t>(nr);
         p.K = static_cast<int32_t>(K);
         p.N = static_cast<int32_t>(N);
