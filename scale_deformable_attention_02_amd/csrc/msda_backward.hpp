@@ -174,7 +174,7 @@ struct DedupShared {
     uint32_t offs[kDedupSlots + 1];
 };
 
-struct DedupEntry {
+struct __align__(8) DedupEntry {
     float aw;      // A * w_c
     uint32_t gi;   // float offset of the sample's output-gradient row in the workgroup's tile
 };
@@ -531,6 +531,8 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
         const int rl = 1 << log2R;               // lanes per row (D <= 64)
         const int ngroups = kThreads / rl;
         const int grp = tid / rl, ch = tid % rl;
+        // lanes past D (D not a power of two) read channel D-1 and never store
+        const uint32_t chc = static_cast<uint32_t>(min(ch, D - 1));
         const float* gflat = &gtile[0][0];
         for (int l = 0; l < p.L; ++l) {
             const int base = dd.base[l];
@@ -542,11 +544,26 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
             for (int local = grp; local < rows; local += ngroups) {
                 const uint32_t b0 = dd.offs[base + local], b1 = dd.offs[base + local + 1];
                 if (b0 == b1) continue;
-                float acc = 0.0f;
-                for (uint32_t e = b0; e < b1; ++e) {
-                    const DedupEntry en = list[e];
-                    acc = fmaf(en.aw, ch < D ? gflat[en.gi + static_cast<uint32_t>(ch)] : 0.0f, acc);
+                // four entries per round: their eight LDS reads overlap
+                float acc0 = 0.0f, acc1 = 0.0f;
+                uint32_t e = b0;
+                for (; e + 4u <= b1; e += 4u) {
+                    DedupEntry en[4];
+                    float gv[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) en[u] = list[e + u];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) gv[u] = gflat[en[u].gi + chc];
+                    acc0 = fmaf(en[0].aw, gv[0], acc0);
+                    acc1 = fmaf(en[1].aw, gv[1], acc1);
+                    acc0 = fmaf(en[2].aw, gv[2], acc0);
+                    acc1 = fmaf(en[3].aw, gv[3], acc1);
                 }
+                for (; e < b1; ++e) {
+                    const DedupEntry en = list[e];
+                    acc0 = fmaf(en.aw, gflat[en.gi + chc], acc0);
+                }
+                const float acc = acc0 + acc1;
                 const uint32_t y = fast_div(static_cast<uint32_t>(local), dw);
                 const uint32_t x = static_cast<uint32_t>(local) - y * static_cast<uint32_t>(ww);
                 const uint32_t pix = (static_cast<uint32_t>(oy) + y) * static_cast<uint32_t>(lg.W) +
