@@ -28,7 +28,7 @@
 #endif
 
 // Backward: workgroups of kDedupWaves waves of one (image, head) slice sum
-// the contributions to each grad_value row before the atomics (2D, D <= 64,
+// the contributions to each grad_value row before the atomics (D <= 64,
 // launches of at least MSDA_DEDUP_MIN_TILES tiles).
 #ifndef MSDA_DEDUP_MIN_TILES
 #define MSDA_DEDUP_MIN_TILES 65536
@@ -279,13 +279,10 @@ int forward(const void* value, int value_dtype, const int64_t* spatial_shapes,
 
 template <typename TV, typename TG, int DIM, int CPL>
 void launch_bwd_one(const msda::BwdParams& bp, hipStream_t stream) {
-    if constexpr (DIM == 2) {
-        if (bp.dedup) {
-            hipLaunchKernelGGL((msda::msda_backward_kernel<TV, TG, DIM, CPL, kDedupWaves, true>),
-                               dim3(bp.f.num_blocks), dim3(kDedupWaves * msda::kWave), 0, stream,
-                               bp);
-            return;
-        }
+    if (bp.dedup) {
+        hipLaunchKernelGGL((msda::msda_backward_kernel<TV, TG, DIM, CPL, kDedupWaves, true>),
+                           dim3(bp.f.num_blocks), dim3(kDedupWaves * msda::kWave), 0, stream, bp);
+        return;
     }
     hipLaunchKernelGGL((msda::msda_backward_kernel<TV, TG, DIM, CPL>), dim3(bp.f.num_blocks),
                        dim3(msda::kBlockThreads), 0, stream, bp);
@@ -405,9 +402,10 @@ int backward(const void* value, int value_dtype, const int64_t* spatial_shapes,
         for (int64_t q0 = 0; q0 < Lq; q0 += nq) {
             const int64_t nquery = (Lq - q0 < nq) ? Lq - q0 : nq;
             // de-duplication: workgroups of kDedupWaves waves that stay in
-            // one slice (waves per slice padded to a multiple)
-            const bool dedup = DIM == 2 && D <= 64 &&
-                               nbatch * M * nquery >= MSDA_DEDUP_MIN_TILES;
+            // one slice (waves per slice padded to a multiple), when a wave's
+            // output-gradient rows fit its LDS tile
+            const bool dedup = D <= 64 && nbatch * M * nquery >= MSDA_DEDUP_MIN_TILES &&
+                               T * D <= msda::grad_tile_floats<DIM, true>();
             const int64_t wave_group = dedup ? kDedupWaves : msda::kWavesPerBlock;
             int64_t waves_per_slice = (nquery + T - 1) / T;
             if (dedup) waves_per_slice = (waves_per_slice + wave_group - 1) / wave_group * wave_group;

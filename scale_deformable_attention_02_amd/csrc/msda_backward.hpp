@@ -45,9 +45,12 @@ struct BwdParams {
     uint32_t dedup;              // 1: the de-duplicating workgroups run
 };
 
-// Output-gradient rows of one wave's tiles: T * D floats <= 64 * 16 / sizeof(value)
-// bytes / 4 (at most T * CPL * 16 bytes of value channels, 8 per chunk for bf16).
-constexpr int kGradTileFloats = 512;
+// Output-gradient rows of one wave's tiles in LDS: T * D floats, at most
+// T * CPL * 16 bytes of value channels (256 floats for fp32 values, 512 for
+// bf16).  The 3D de-duplicating kernel, whose slots are larger, holds 256 per
+// wave; its launches need T * D <= 256.
+template <int DIM, bool DEDUP>
+constexpr int grad_tile_floats() { return DEDUP && DIM == 3 ? 256 : 512; }
 
 // Everything phase B needs about one sample.
 template <int NC, int DIM>
@@ -153,20 +156,22 @@ __device__ __forceinline__ void load_grad(__amdgpu_buffer_rsrc_t r, uint32_t off
 // collect contributions for (slot tables of 4 B counts and offsets).
 constexpr int kDedupSlots = 4096;
 
-// FastDiv built on the device (the host's construction): exact for x < 2^31.
-__device__ __forceinline__ FastDiv make_fast_div_dev(uint32_t d) {
-    uint32_t l = 0;
-    while ((1ull << l) < d) ++l;
-    const uint64_t shift = 31 + l;
-    const uint64_t mul = ((1ull << shift) + d - 1) / d;
-    return FastDiv{static_cast<uint32_t>(mul), static_cast<uint32_t>(shift)};
+// floor(x / d) for x < 2^24, d >= 1, from rcp = 1.0f / d: x * rcp is within
+// one of x / d (both exact below 2^24, rcp within 2^-24 relative), so one
+// correction step makes it exact.
+__device__ __forceinline__ uint32_t div_small(uint32_t x, uint32_t d, float rcp) {
+    uint32_t q = static_cast<uint32_t>(static_cast<float>(x) * rcp);
+    if (q * d > x) --q;
+    else if ((q + 1u) * d <= x) ++q;
+    return q;
 }
 
 struct DedupShared {
-    uint32_t bbox[kMaxLevels][4];   // per level: ~min x, ~min y, max x, max y (max-reduced)
+    uint32_t bbox[kMaxLevels][6];   // per level: ~min x, y, z, max x, y, z (max-reduced)
     int base[kMaxLevels];           // first slot of the level's window, or -1
-    int ox[kMaxLevels], oy[kMaxLevels], ww[kMaxLevels], rows[kMaxLevels];
-    FastDiv div_ww[kMaxLevels];
+    int ox[kMaxLevels], oy[kMaxLevels], oz[kMaxLevels];   // window origin
+    int ww[kMaxLevels], hh[kMaxLevels], rows[kMaxLevels]; // width, height, slots
+    float rcp_ww[kMaxLevels], rcp_hh[kMaxLevels];
     int nslots;
     int any_direct;                 // some level takes the direct atomics of phase C
     uint32_t wave_sum[16];
@@ -180,28 +185,40 @@ struct __align__(8) DedupEntry {
 };
 
 // Integer cell of a sample (same arithmetic as make_bwd_slot): whether it
-// touches the level, and floor of its pixel-space coordinates.
+// touches the level, and floor of its pixel-space coordinates (z0 = 0 in 2D).
 template <int DIM>
 __device__ __forceinline__ bool bwd_cell(const float (&xyz)[DIM], bool live, const LevelGeom& lg,
-                                         int& x0, int& y0) {
+                                         int& x0, int& y0, int& z0) {
     const float Wf = static_cast<float>(lg.W), Hf = static_cast<float>(lg.H);
     const float xh = fmaf(xyz[0], Wf, -0.5f);
     const float yh = fmaf(xyz[1], Hf, -0.5f);
     bool inside = live && xh > -1.0f && xh < Wf && yh > -1.0f && yh < Hf;
+    z0 = 0;
     if constexpr (DIM == 3) {
         const float Zf = static_cast<float>(lg.Z);
         const float zh = fmaf(xyz[2], Zf, -0.5f);
         inside = inside && zh > -1.0f && zh < Zf;
+        z0 = inside ? static_cast<int>(floorf(zh)) : 0;
     }
     x0 = inside ? static_cast<int>(floorf(xh)) : 0;
     y0 = inside ? static_cast<int>(floorf(yh)) : 0;
     return inside;
 }
 
-// WAVES waves per workgroup.  DEDUP (2D, D <= 64, WAVES consecutive waves of
-// one (image, head) slice): contributions to grad_value rows that several
-// samples of the workgroup touch are summed in registers before one atomic
-// row update (see phase D).
+// LDS of the de-duplicating kernel (at most 160 KB per workgroup).
+template <int DIM, int WAVES>
+constexpr size_t bwd_dedup_lds() {
+    return sizeof(LevelGeom) * kMaxSamplesPerTile +
+           sizeof(BwdSlot<DIM == 2 ? 4 : 8, DIM>) * WAVES * kWave + sizeof(DedupShared) +
+           sizeof(float) * WAVES * grad_tile_floats<DIM, true>();
+}
+static_assert(bwd_dedup_lds<2, 16>() + 512 <= 160 * 1024 && bwd_dedup_lds<3, 16>() + 512 <= 160 * 1024,
+              "de-duplicating workgroups of 16 waves fit the LDS");
+
+// WAVES waves per workgroup.  DEDUP (D <= 64, WAVES consecutive waves of one
+// (image, head) slice): contributions to grad_value rows that several samples
+// of the workgroup touch are summed in registers before one atomic row update
+// (see phase D).
 template <typename TV, typename TG, int DIM, int CPL, int WAVES = kWavesPerBlock,
           bool DEDUP = false>
 __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams bp) {
@@ -209,13 +226,16 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
     constexpr int NG = kWave / CPL;
     constexpr int VEC = ValueTraits<TV>::kVec;
     constexpr int kThreads = WAVES * kWave;
-    static_assert(!DEDUP || (DIM == 2 && 4 * kThreads >= kDedupSlots),
-                  "de-duplication: 2D, four table slots per thread at most");
+    static_assert(!DEDUP || 4 * kThreads >= kDedupSlots,
+                  "de-duplication: four table slots per thread at most");
+    static_assert(!DEDUP || sizeof(BwdSlot<NC, DIM>) >= NC * sizeof(DedupEntry),
+                  "de-duplication: the entry lists reuse the slot array");
     const Params& p = bp.f;
 
     __shared__ LevelGeom smeta[kMaxSamplesPerTile];
     __shared__ BwdSlot<NC, DIM> slots[WAVES][kWave];
-    __shared__ float gtile[WAVES][kGradTileFloats];
+    constexpr int kTile = grad_tile_floats<DIM, DEDUP>();
+    __shared__ float gtile_all[WAVES * kTile];
     using DedupT = typename std::conditional<DEDUP, DedupShared, int>::type;
     __shared__ DedupT dd;
 
@@ -235,7 +255,7 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
 
     if constexpr (DEDUP) {
         for (int i = tid; i < kDedupSlots; i += kThreads) dd.count[i] = 0u;
-        if (tid < kMaxLevels * 4) (&dd.bbox[0][0])[tid] = 0u;   // ~min = 0 means +inf
+        if (tid < kMaxLevels * 6) (&dd.bbox[0][0])[tid] = 0u;   // ~min = 0 means +inf
     }
 
     const uint32_t blk = xcd_contiguous_block(blockIdx.x, p.num_blocks);
@@ -249,10 +269,11 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
     const uint32_t row0 = (n * static_cast<uint32_t>(p.Lq) + q0) * static_cast<uint32_t>(p.M) + m;
     const uint32_t ghead_base = n * gimage_bytes + m * ghead_bytes;
     const int G = 1 << p.log2G;
+    float* gtile = gtile_all + wave * kTile;   // this wave's tiles' gradient rows
 
     // ---- Phase A: lane k fills slot k = i*NG + g.
     BwdSlot<NC, DIM> mine;           // this lane's sample (kept for phase D)
-    int my_level = 0, my_x0 = 0, my_y0 = 0, my_tile = 0;
+    int my_level = 0, my_x0 = 0, my_y0 = 0, my_z0 = 0, my_tile = 0;
     bool my_in = false;
     {
         const int i = lane / NG, g = lane % NG;
@@ -272,8 +293,8 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
         slots[wave][lane] = mine;
         if constexpr (DEDUP) {
             my_level = static_cast<int>(fast_div(static_cast<uint32_t>(s_c), p.div_P));
-            my_in = bwd_cell<DIM>(xyz, live, lg, my_x0, my_y0) && mine.a != 0.0f;
-            my_tile = wave * kGradTileFloats + t * p.nchunk * VEC;
+            my_in = bwd_cell<DIM>(xyz, live, lg, my_x0, my_y0, my_z0) && mine.a != 0.0f;
+            my_tile = wave * kTile + t * p.nchunk * VEC;
         }
     }
     __syncthreads();
@@ -301,7 +322,7 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
         load_grad<TG, VEC>(rgo, goff, gch);
         if ((g & (G - 1)) == 0 && chunk_live) {
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) gtile[wave][t * D + c * VEC + e] = gch[e];
+            for (int e = 0; e < VEC; ++e) gtile[t * D + c * VEC + e] = gch[e];
         }
     }
 
@@ -372,57 +393,68 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
     // windows fit kDedupSlots (smallest first) collect their contributions
     // per pixel row.  Other levels keep the direct atomics of phase C.
     if constexpr (DEDUP) {
+        constexpr int NB = DIM == 2 ? 4 : 6;   // box values: ~min x, y(, z), max x, y(, z)
         for (int l = 0; l < p.L; ++l) {
-            uint32_t v[4];
             const bool mine_l = my_in && my_level == l;
-            v[0] = mine_l ? ~static_cast<uint32_t>(max(my_x0, 0)) : 0u;
-            v[1] = mine_l ? ~static_cast<uint32_t>(max(my_y0, 0)) : 0u;
-            v[2] = mine_l ? static_cast<uint32_t>(min(my_x0 + 1, smeta[l * p.P].W - 1)) : 0u;
-            v[3] = mine_l ? static_cast<uint32_t>(min(my_y0 + 1, smeta[l * p.P].H - 1)) : 0u;
+            const LevelGeom lgl = smeta[l * p.P];
+            const int cell[3] = {my_x0, my_y0, my_z0};
+            const int ext[3] = {lgl.W, lgl.H, lgl.Z};
+            uint32_t v[6];
+#pragma unroll
+            for (int a = 0; a < DIM; ++a) {
+                v[a] = mine_l ? ~static_cast<uint32_t>(max(cell[a], 0)) : 0u;
+                v[DIM + a] = mine_l ? static_cast<uint32_t>(min(cell[a] + 1, ext[a] - 1)) : 0u;
+            }
 #pragma unroll
             for (int b = 1; b < kWave; b <<= 1)
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
+                for (int e = 0; e < NB; ++e)
                     v[e] = max(v[e], static_cast<uint32_t>(__shfl_xor(static_cast<int>(v[e]), b, kWave)));
             if (lane == 0 && v[0] != 0u) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) atomicMax(&dd.bbox[l][e], v[e]);
+                for (int a = 0; a < DIM; ++a) {
+                    atomicMax(&dd.bbox[l][a], v[a]);
+                    atomicMax(&dd.bbox[l][3 + a], v[DIM + a]);
+                }
             }
         }
         __syncthreads();
         if (tid < p.L) {
-            const uint32_t lo_x = ~dd.bbox[tid][0], lo_y = ~dd.bbox[tid][1];
-            const uint32_t hi_x = dd.bbox[tid][2], hi_y = dd.bbox[tid][3];
             const bool any = dd.bbox[tid][0] != 0u;
-            const int w = any ? static_cast<int>(hi_x - lo_x) + 1 : 0;
-            const int h = any ? static_cast<int>(hi_y - lo_y) + 1 : 0;
-            dd.ox[tid] = static_cast<int>(lo_x);
-            dd.oy[tid] = static_cast<int>(lo_y);
-            dd.ww[tid] = w > 0 ? w : 1;
-            dd.rows[tid] = w * h;
+            int lo[3] = {0, 0, 0}, ext[3] = {1, 1, 1};
+#pragma unroll
+            for (int a = 0; a < DIM; ++a) {
+                lo[a] = static_cast<int>(~dd.bbox[tid][a]);
+                ext[a] = any ? static_cast<int>(dd.bbox[tid][3 + a]) - lo[a] + 1 : 0;
+            }
+            dd.ox[tid] = lo[0];
+            dd.oy[tid] = lo[1];
+            dd.oz[tid] = lo[2];
+            dd.ww[tid] = ext[0] > 0 ? ext[0] : 1;
+            dd.hh[tid] = ext[1] > 0 ? ext[1] : 1;
+            dd.rcp_ww[tid] = 1.0f / static_cast<float>(dd.ww[tid]);
+            dd.rcp_hh[tid] = 1.0f / static_cast<float>(dd.hh[tid]);
+            dd.rows[tid] = ext[0] * ext[1] * ext[2];
+        }
+        if (tid == 0) {
+            dd.nslots = 0;
+            dd.any_direct = 0;
         }
         __syncthreads();
-        if (tid == 0) {
+        if (tid < p.L) {
             // windows in ascending size (ties by level) while the total fits
             // the table; the total only grows, so a level that does not fit
             // excludes every larger one
-            int nslots = 0;
-            for (int l = 0; l < p.L; ++l) {
-                const int mine_rows = dd.rows[l];
-                int before = 0;
-                for (int k = 0; k < p.L; ++k) {
-                    const int r = dd.rows[k];
-                    if (r < mine_rows || (r == mine_rows && k < l)) before += r;
-                }
-                const bool fits = mine_rows > 0 && before + mine_rows <= kDedupSlots;
-                dd.base[l] = fits ? before : -1;
-                dd.div_ww[l] = make_fast_div_dev(static_cast<uint32_t>(dd.ww[l]));
-                if (fits) nslots = max(nslots, before + mine_rows);
+            const int mine_rows = dd.rows[tid];
+            int before = 0;
+            for (int k = 0; k < p.L; ++k) {
+                const int r = dd.rows[k];
+                if (r < mine_rows || (r == mine_rows && k < tid)) before += r;
             }
-            dd.nslots = nslots;
-            int any = 0;
-            for (int l = 0; l < p.L; ++l) any |= dd.base[l] < 0 && dd.rows[l] > 0 ? 1 : 0;
-            dd.any_direct = any;
+            const bool fits = mine_rows > 0 && before + mine_rows <= kDedupSlots;
+            dd.base[tid] = fits ? before : -1;
+            if (fits) atomicMax(&dd.nslots, before + mine_rows);
+            if (!fits && mine_rows > 0) atomicOr(&dd.any_direct, 1);
         }
         __syncthreads();
     }
@@ -457,7 +489,7 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
         }
         if (direct && d < static_cast<uint32_t>(D) && off != kOutOfRange && a != 0.0f) {
             const int ts = static_cast<int>(sig & (NG - 1)) >> log2G;
-            const float gd = gtile[wave][ts * D + static_cast<int>(d)];
+            const float gd = gtile[ts * D + static_cast<int>(d)];
             __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(a * sp->w[k] * gd, rgv, off + 4u * d,
                                                             0, 0);
         }
@@ -475,12 +507,13 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
         for (int k = 0; k < NC; ++k) {
             slot_id[k] = 0xffffffffu;
             pos[k] = 0u;
-            const int cx = k & 1, cy = (k >> 1) & 1;
+            const int cx = k & 1, cy = (k >> 1) & 1, cz = k >> 2;
             const int base = dd.base[my_level];
             if (my_in && base >= 0 && mine.off[k] != kOutOfRange) {
                 const int x = my_x0 + cx - dd.ox[my_level];
                 const int y = my_y0 + cy - dd.oy[my_level];
-                slot_id[k] = static_cast<uint32_t>(base + y * dd.ww[my_level] + x);
+                const int z = my_z0 + cz - dd.oz[my_level];
+                slot_id[k] = static_cast<uint32_t>(base + (z * dd.hh[my_level] + y) * dd.ww[my_level] + x);
                 pos[k] = atomicAdd(&dd.count[slot_id[k]], 1u);
             }
         }
@@ -533,13 +566,13 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
         const int grp = tid / rl, ch = tid % rl;
         // lanes past D (D not a power of two) read channel D-1 and never store
         const uint32_t chc = static_cast<uint32_t>(min(ch, D - 1));
-        const float* gflat = &gtile[0][0];
+        const float* gflat = gtile_all;
         for (int l = 0; l < p.L; ++l) {
             const int base = dd.base[l];
             if (base < 0) continue;
             const int rows = dd.rows[l];
-            const int ww = dd.ww[l], ox = dd.ox[l], oy = dd.oy[l];
-            const FastDiv dw = dd.div_ww[l];
+            const int ww = dd.ww[l], hh = dd.hh[l], ox = dd.ox[l], oy = dd.oy[l], oz = dd.oz[l];
+            const float rw = dd.rcp_ww[l], rh = dd.rcp_hh[l];
             const LevelGeom lg = smeta[l * p.P];
             for (int local = grp; local < rows; local += ngroups) {
                 const uint32_t b0 = dd.offs[base + local], b1 = dd.offs[base + local + 1];
@@ -564,9 +597,13 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
                     acc0 = fmaf(en.aw, gflat[en.gi + chc], acc0);
                 }
                 const float acc = acc0 + acc1;
-                const uint32_t y = fast_div(static_cast<uint32_t>(local), dw);
-                const uint32_t x = static_cast<uint32_t>(local) - y * static_cast<uint32_t>(ww);
-                const uint32_t pix = (static_cast<uint32_t>(oy) + y) * static_cast<uint32_t>(lg.W) +
+                // window slot -> (z, y, x) of the level (z = 0 in 2D)
+                const uint32_t zy = div_small(static_cast<uint32_t>(local), static_cast<uint32_t>(ww), rw);
+                const uint32_t x = static_cast<uint32_t>(local) - zy * static_cast<uint32_t>(ww);
+                const uint32_t z = DIM == 3 ? div_small(zy, static_cast<uint32_t>(hh), rh) : 0u;
+                const uint32_t y = zy - z * static_cast<uint32_t>(hh);
+                const uint32_t pix = ((static_cast<uint32_t>(oz) + z) * static_cast<uint32_t>(lg.H) +
+                                      static_cast<uint32_t>(oy) + y) * static_cast<uint32_t>(lg.W) +
                                      static_cast<uint32_t>(ox) + x;
                 const uint32_t off = ghead_base + lg.start_bytes + pix * grow_bytes;
                 if (ch < D)

@@ -37,4 +37,7 @@ STAGED = [
     (2, "f32", 1, ((300, 300),), 70001, 1, 4, 4, "uniform"),     # no level fits
     (3, "f32", 2, ((16, 16, 16), (8, 8, 8), (4, 4, 4)), 4672, 8, 32, 4, "pixel_centres"),
     (3, "bf16", 1, ((16, 16, 16), (8, 8, 8), (4, 4, 4)), 9000, 8, 32, 2, "random_refs"),
+    # bf16, 64 channels, L*P = 8: the backward's de-duplicating workgroups
+    # would not fit the LDS (8 tiles per wave), so it takes the direct path
+    (3, "bf16", 1, ((16, 16, 16), (8, 8, 8)), 8300, 8, 64, 4, "random_refs"),
 ]
