@@ -10,8 +10,10 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libmsda.so")
-SOURCES = [os.path.join(CSRC, "msda_api.hip"), os.path.join(CSRC, "msda_linear.hip")]
+SOURCES = [os.path.join(CSRC, "msda_api.hip"), os.path.join(CSRC, "msda_backward_api.hip"),
+           os.path.join(CSRC, "msda_linear.hip")]
 DEPENDS = SOURCES + [os.path.join(CSRC, "msda_device.hpp"), os.path.join(CSRC, "msda_backward.hpp"),
+                     os.path.join(CSRC, "msda_host.hpp"),
                      os.path.join(INCLUDE, "msda.h")]
 
 ARCH = "gfx950"
@@ -38,14 +40,31 @@ def compile_flags(extra=()):
 
 
 def build(verbose: bool = False, extra=()) -> str:
-    """Compile ``libmsda.so`` (always rebuilds); returns its path."""
+    """Compile ``libmsda.so`` (always rebuilds); returns its path.
+
+    Each translation unit is compiled by its own hipcc process (in parallel),
+    then the objects are linked."""
+    import concurrent.futures
+    import tempfile
+
     tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), *compile_flags(extra), "-shared", "-o", tmp, *SOURCES]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    proc = subprocess.run(cmd, capture_output=True, text=True)
-    if proc.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({proc.returncode}):\n{proc.stderr}")
+    with tempfile.TemporaryDirectory(prefix="msda_build_") as work:
+        objs = [os.path.join(work, os.path.splitext(os.path.basename(src))[0] + ".o")
+                for src in SOURCES]
+        cmds = [[hipcc(), *compile_flags(extra), "-c", "-o", obj, src]
+                for src, obj in zip(SOURCES, objs)]
+        cmds.append([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
+
+        def run(cmd):
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            proc = subprocess.run(cmd, capture_output=True, text=True)
+            if proc.returncode != 0:
+                raise RuntimeError(f"hipcc failed ({proc.returncode}):\n{proc.stderr}")
+
+        with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as pool:
+            list(pool.map(run, cmds[:-1]))
+        run(cmds[-1])
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 
