@@ -612,8 +612,14 @@ struct StagedParams {
     int32_t ipl;             // phase-B iterations per level, P / G
 };
 
+// Two 16-wave workgroups per CU need 8 waves per SIMD, i.e. at most 64 VGPRs.
+// Every variant is held to that except the pruned one on bf16 values, which
+// would spill 40 bytes per lane there and measured slower than one workgroup
+// per CU (the fp32 pruned variant spills 20 bytes and gains).
 template <typename TV, typename TO, int DIM, int CPL, bool FUSED = false, bool PRUNE = false>
-__global__ __launch_bounds__(kStagedThreads) void msda_forward_staged_kernel(StagedParams sp) {
+__global__ __launch_bounds__(kStagedThreads)
+__attribute__((amdgpu_waves_per_eu(PRUNE && sizeof(TV) == 2 ? 1 : 8)))
+void msda_forward_staged_kernel(StagedParams sp) {
     constexpr int NC = DIM == 2 ? 4 : 8;
     constexpr int NG = kWave / CPL;
     constexpr int VEC = ValueTraits<TV>::kVec;
