@@ -50,7 +50,7 @@ struct BwdParams {
 // bf16).  The 3D de-duplicating kernel, whose slots are larger, holds 256 per
 // wave; its launches need T * D <= 256.
 template <int DIM, bool DEDUP>
-constexpr int grad_tile_floats() { return DEDUP && DIM == 3 ? 256 : 512; }
+constexpr int grad_tile_floats() { return DEDUP ? 256 : 512; }
 
 // Everything phase B needs about one sample.
 template <int NC, int DIM>
@@ -58,7 +58,6 @@ struct __align__(16) BwdSlot {
     uint32_t off[NC];   // byte offsets of the corner rows in grad_value (fp32)
     float w[NC];        // pure interpolation weights (0 for corners outside)
     float frac[DIM];    // fx, fy (, fz)
-    float ext[DIM];     // W, H (, Z) as floats: d x_hat / d x
     float a;            // attention weight (0 for a dead or outside sample)
     uint32_t sidx;      // sample index in this launch, or kNoSample
 };
@@ -108,12 +107,7 @@ __device__ __forceinline__ BwdSlot<DIM == 2 ? 4 : 8, DIM> make_bwd_slot(
     }
     sl.frac[0] = fx;
     sl.frac[1] = fy;
-    sl.ext[0] = Wf;
-    sl.ext[1] = Hf;
-    if constexpr (DIM == 3) {
-        sl.frac[2] = fz;
-        sl.ext[2] = Zf;
-    }
+    if constexpr (DIM == 3) sl.frac[2] = fz;
     sl.a = inside ? a : 0.0f;
     sl.sidx = live ? sidx : kNoSample;
     return sl;
@@ -153,8 +147,11 @@ __device__ __forceinline__ void load_grad(__amdgpu_buffer_rsrc_t r, uint32_t off
 }
 
 // Rows of grad_value per workgroup that the de-duplicating variant can
-// collect contributions for (slot tables of 4 B counts and offsets).
-constexpr int kDedupSlots = 4096;
+// collect contributions for (tables of 16-bit counts and list offsets).  2D:
+// sized so that two workgroups share a CU's LDS; 3D (one workgroup per CU,
+// larger slots): the finer levels' voxel boxes need more.
+template <int DIM>
+constexpr int dedup_slots() { return DIM == 2 ? 3072 : 4096; }
 
 // floor(x / d) for x < 2^24, d >= 1, from rcp = 1.0f / d: x * rcp is within
 // one of x / d (both exact below 2^24, rcp within 2^-24 relative), so one
@@ -166,6 +163,7 @@ __device__ __forceinline__ uint32_t div_small(uint32_t x, uint32_t d, float rcp)
     return q;
 }
 
+template <int SLOTS>
 struct DedupShared {
     uint32_t bbox[kMaxLevels][6];   // per level: ~min x, y, z, max x, y, z (max-reduced)
     int base[kMaxLevels];           // first slot of the level's window, or -1
@@ -175,8 +173,8 @@ struct DedupShared {
     int nslots;
     int any_direct;                 // some level takes the direct atomics of phase C
     uint32_t wave_sum[16];
-    uint32_t count[kDedupSlots];
-    uint32_t offs[kDedupSlots + 1];
+    uint32_t count2[SLOTS / 2];   // 16-bit counts, two slots per word
+    uint16_t offs[SLOTS + 2];     // list start of each slot, then the total
 };
 
 struct __align__(8) DedupEntry {
@@ -209,11 +207,16 @@ __device__ __forceinline__ bool bwd_cell(const float (&xyz)[DIM], bool live, con
 template <int DIM, int WAVES>
 constexpr size_t bwd_dedup_lds() {
     return sizeof(LevelGeom) * kMaxSamplesPerTile +
-           sizeof(BwdSlot<DIM == 2 ? 4 : 8, DIM>) * WAVES * kWave + sizeof(DedupShared) +
+           sizeof(BwdSlot<DIM == 2 ? 4 : 8, DIM>) * WAVES * kWave +
+           sizeof(DedupShared<dedup_slots<DIM>()>) +
            sizeof(float) * WAVES * grad_tile_floats<DIM, true>();
 }
-static_assert(bwd_dedup_lds<2, 16>() + 512 <= 160 * 1024 && bwd_dedup_lds<3, 16>() + 512 <= 160 * 1024,
-              "de-duplicating workgroups of 16 waves fit the LDS");
+static_assert(bwd_dedup_lds<2, 16>() + 512 <= 80 * 1024,
+              "two 2D de-duplicating workgroups of 16 waves share a CU's 160 KB of LDS");
+static_assert(bwd_dedup_lds<3, 16>() + 512 <= 160 * 1024,
+              "a 3D de-duplicating workgroup of 16 waves fits the LDS");
+static_assert(16 * kWave * 8 < 65536 && dedup_slots<2>() % 4 == 0 && dedup_slots<3>() % 4 == 0,
+              "16-bit counts and list offsets; four table slots per scan thread");
 
 // WAVES waves per workgroup.  DEDUP (D <= 64, WAVES consecutive waves of one
 // (image, head) slice): contributions to grad_value rows that several samples
@@ -226,6 +229,7 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
     constexpr int NG = kWave / CPL;
     constexpr int VEC = ValueTraits<TV>::kVec;
     constexpr int kThreads = WAVES * kWave;
+    constexpr int kDedupSlots = dedup_slots<DIM>();
     static_assert(!DEDUP || 4 * kThreads >= kDedupSlots,
                   "de-duplication: four table slots per thread at most");
     static_assert(!DEDUP || sizeof(BwdSlot<NC, DIM>) >= NC * sizeof(DedupEntry),
@@ -236,7 +240,7 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
     __shared__ BwdSlot<NC, DIM> slots[WAVES][kWave];
     constexpr int kTile = grad_tile_floats<DIM, DEDUP>();
     __shared__ float gtile_all[WAVES * kTile];
-    using DedupT = typename std::conditional<DEDUP, DedupShared, int>::type;
+    using DedupT = typename std::conditional<DEDUP, DedupShared<kDedupSlots>, int>::type;
     __shared__ DedupT dd;
 
     const int tid = threadIdx.x;
@@ -254,7 +258,7 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
     }
 
     if constexpr (DEDUP) {
-        for (int i = tid; i < kDedupSlots; i += kThreads) dd.count[i] = 0u;
+        for (int i = tid; i < kDedupSlots / 2; i += kThreads) dd.count2[i] = 0u;
         if (tid < kMaxLevels * 6) (&dd.bbox[0][0])[tid] = 0u;   // ~min = 0 means +inf
     }
 
@@ -350,15 +354,19 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
             for (int s = 1; s < CPL; s <<= 1) dot[k] += __shfl_xor(dot[k], s, kWave);
 
         if (c == 0 && sl.sidx != kNoSample) {
+            // d x_hat / d x = W (, H, Z) of the sample's level
+            const LevelGeom lgs = smeta[min(i * G + (g & (G - 1)), p.LP - 1)];
+            const float ext[3] = {static_cast<float>(lgs.W), static_cast<float>(lgs.H),
+                                  static_cast<float>(lgs.Z)};
             float da = 0.0f;
 #pragma unroll
             for (int k = 0; k < NC; ++k) da = fmaf(sl.w[k], dot[k], da);
             float gl[DIM];
             if constexpr (DIM == 2) {
                 const float fx = sl.frac[0], fy = sl.frac[1];
-                gl[0] = sl.a * sl.ext[0] *
+                gl[0] = sl.a * ext[0] *
                         ((1.0f - fy) * (dot[1] - dot[0]) + fy * (dot[3] - dot[2]));
-                gl[1] = sl.a * sl.ext[1] *
+                gl[1] = sl.a * ext[1] *
                         ((1.0f - fx) * (dot[2] - dot[0]) + fx * (dot[3] - dot[1]));
             } else {
                 const float f[3] = {sl.frac[0], sl.frac[1], sl.frac[2]};
@@ -379,7 +387,7 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
                     }
                 }
 #pragma unroll
-                for (int d = 0; d < 3; ++d) gl[d] = sl.a * sl.ext[d] * g3[d];
+                for (int d = 0; d < 3; ++d) gl[d] = sl.a * ext[d] * g3[d];
             }
             // a sample outside the support has a = 0 and all weights 0: zeros
             bp.grad_attw[sl.sidx] = da;
@@ -514,7 +522,9 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
                 const int y = my_y0 + cy - dd.oy[my_level];
                 const int z = my_z0 + cz - dd.oz[my_level];
                 slot_id[k] = static_cast<uint32_t>(base + (z * dd.hh[my_level] + y) * dd.ww[my_level] + x);
-                pos[k] = atomicAdd(&dd.count[slot_id[k]], 1u);
+                // counts stay below 2^16 (at most WAVES * 64 * NC entries)
+                const uint32_t sh = (slot_id[k] & 1u) * 16u;
+                pos[k] = (atomicAdd(&dd.count2[slot_id[k] >> 1], 1u << sh) >> sh) & 0xffffu;
             }
         }
         __syncthreads();
@@ -524,7 +534,10 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
             const int i0 = 4 * tid;
             uint32_t cv[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) cv[e] = i0 + e < nslots ? dd.count[i0 + e] : 0u;
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t w2 = i0 < kDedupSlots ? dd.count2[(i0 >> 1) + (e >> 1)] : 0u;
+                cv[e] = i0 + e < nslots ? (w2 >> ((e & 1) * 16)) & 0xffffu : 0u;
+            }
             const uint32_t mine_sum = cv[0] + cv[1] + cv[2] + cv[3];
             uint32_t incl = mine_sum;
 #pragma unroll
@@ -539,13 +552,13 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
             uint32_t run = before + incl - mine_sum;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                if (i0 + e < nslots) dd.offs[i0 + e] = run;
+                if (i0 + e < nslots) dd.offs[i0 + e] = static_cast<uint16_t>(run);
                 run += cv[e];
             }
             if (tid == kThreads - 1) {
                 uint32_t all = 0u;
                 for (int w = 0; w < WAVES; ++w) all += dd.wave_sum[w];
-                dd.offs[nslots] = all;
+                dd.offs[nslots] = static_cast<uint16_t>(all);
             }
         }
         __syncthreads();
