@@ -401,29 +401,16 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
     // windows fit kDedupSlots (smallest first) collect their contributions
     // per pixel row.  Other levels keep the direct atomics of phase C.
     if constexpr (DEDUP) {
-        constexpr int NB = DIM == 2 ? 4 : 6;   // box values: ~min x, y(, z), max x, y(, z)
-        for (int l = 0; l < p.L; ++l) {
-            const bool mine_l = my_in && my_level == l;
-            const LevelGeom lgl = smeta[l * p.P];
+        // each lane widens its own level's box (LDS integer atomics; the
+        // minima as maxima of complements)
+        if (my_in) {
+            const LevelGeom lgl = smeta[my_level * p.P];
             const int cell[3] = {my_x0, my_y0, my_z0};
             const int ext[3] = {lgl.W, lgl.H, lgl.Z};
-            uint32_t v[6];
 #pragma unroll
             for (int a = 0; a < DIM; ++a) {
-                v[a] = mine_l ? ~static_cast<uint32_t>(max(cell[a], 0)) : 0u;
-                v[DIM + a] = mine_l ? static_cast<uint32_t>(min(cell[a] + 1, ext[a] - 1)) : 0u;
-            }
-#pragma unroll
-            for (int b = 1; b < kWave; b <<= 1)
-#pragma unroll
-                for (int e = 0; e < NB; ++e)
-                    v[e] = max(v[e], static_cast<uint32_t>(__shfl_xor(static_cast<int>(v[e]), b, kWave)));
-            if (lane == 0 && v[0] != 0u) {
-#pragma unroll
-                for (int a = 0; a < DIM; ++a) {
-                    atomicMax(&dd.bbox[l][a], v[a]);
-                    atomicMax(&dd.bbox[l][3 + a], v[DIM + a]);
-                }
+                atomicMax(&dd.bbox[my_level][a], ~static_cast<uint32_t>(max(cell[a], 0)));
+                atomicMax(&dd.bbox[my_level][3 + a], static_cast<uint32_t>(min(cell[a] + 1, ext[a] - 1)));
             }
         }
         __syncthreads();
