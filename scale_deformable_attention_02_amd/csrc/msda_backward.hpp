@@ -165,13 +165,16 @@ __device__ __forceinline__ uint32_t div_small(uint32_t x, uint32_t d, float rcp)
 
 template <int SLOTS>
 struct DedupShared {
-    uint32_t bbox[kMaxLevels][6];   // per level: ~min x, y, z, max x, y, z (max-reduced)
-    int base[kMaxLevels];           // first slot of the level's window, or -1
-    int ox[kMaxLevels], oy[kMaxLevels], oz[kMaxLevels];   // window origin
-    int ww[kMaxLevels], hh[kMaxLevels], rows[kMaxLevels]; // width, height, slots
-    float rcp_ww[kMaxLevels], rcp_hh[kMaxLevels];
+    // two windows per level (x < W/2, x >= W/2), window w = 2 * level + side
+    uint32_t bbox[2 * kMaxLevels][6];   // ~min x, y, z, max x, y, z (max-reduced)
+    int base[2 * kMaxLevels];           // first slot of the window, or -1
+    int ox[2 * kMaxLevels], oy[2 * kMaxLevels], oz[2 * kMaxLevels];     // origin
+    int ww[2 * kMaxLevels], hh[2 * kMaxLevels], rows[2 * kMaxLevels];  // width, height, slots
+    float rcp_ww[2 * kMaxLevels], rcp_hh[2 * kMaxLevels];
     int nslots;
-    int any_direct;                 // some level takes the direct atomics of phase C
+    int nnz;                        // non-empty slots
+    int nz_begin[2 * kMaxLevels], nz_end[2 * kMaxLevels];   // window's part of the compact list
+    int any_direct;                 // some corners take the direct atomics of phase C
     uint32_t wave_sum[16];
     uint32_t count2[SLOTS / 2];   // 16-bit counts, two slots per word
     uint16_t offs[SLOTS + 2];     // list start of each slot, then the total
@@ -232,8 +235,9 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
     constexpr int kDedupSlots = dedup_slots<DIM>();
     static_assert(!DEDUP || 4 * kThreads >= kDedupSlots,
                   "de-duplication: four table slots per thread at most");
-    static_assert(!DEDUP || sizeof(BwdSlot<NC, DIM>) >= NC * sizeof(DedupEntry),
-                  "de-duplication: the entry lists reuse the slot array");
+    static_assert(!DEDUP || sizeof(BwdSlot<NC, DIM>) * WAVES * kWave >=
+                                NC * sizeof(DedupEntry) * WAVES * kWave + 4 * (kDedupSlots + 1),
+                  "de-duplication: the entry lists and the compact slot list reuse the slot array");
     const Params& p = bp.f;
 
     __shared__ LevelGeom smeta[kMaxSamplesPerTile];
@@ -259,7 +263,7 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
 
     if constexpr (DEDUP) {
         for (int i = tid; i < kDedupSlots / 2; i += kThreads) dd.count2[i] = 0u;
-        if (tid < kMaxLevels * 6) (&dd.bbox[0][0])[tid] = 0u;   // ~min = 0 means +inf
+        if (tid < 2 * kMaxLevels * 6) (&dd.bbox[0][0])[tid] = 0u;   // ~min = 0 means +inf
     }
 
     const uint32_t blk = xcd_contiguous_block(blockIdx.x, p.num_blocks);
@@ -396,25 +400,42 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
         }
     }
 
-    // ---- Phase D1 (de-duplication): each level's window is the bounding box
-    // of the pixels its samples' cells cover in this workgroup; levels whose
-    // windows fit kDedupSlots (smallest first) collect their contributions
-    // per pixel row.  Other levels keep the direct atomics of phase C.
+    // ---- Phase D1 (de-duplication): every level has two windows, the
+    // bounding boxes of the pixels its samples' corners cover in this
+    // workgroup with x < W/2 and with x >= W/2 (a run of queries that wraps
+    // from one image row to the next makes two compact boxes, not one box as
+    // wide as the image).  Windows that fit the slot table (smallest first)
+    // collect their contributions per pixel; the other corners keep the
+    // direct atomics of phase C.
+    uint32_t slot_id[NC], pos[NC];   // D2's table slot and list place of each corner
     if constexpr (DEDUP) {
-        // each lane widens its own level's box (LDS integer atomics; the
+        // each lane widens its own level's boxes (LDS integer atomics; the
         // minima as maxima of complements)
+        const LevelGeom lgl = smeta[my_level * p.P];
+        const int half = lgl.W / 2;
         if (my_in) {
-            const LevelGeom lgl = smeta[my_level * p.P];
-            const int cell[3] = {my_x0, my_y0, my_z0};
-            const int ext[3] = {lgl.W, lgl.H, lgl.Z};
+            const int xa = max(my_x0, 0), xb = min(my_x0 + 1, lgl.W - 1);
+            const int lo_yz[2] = {max(my_y0, 0), max(my_z0, 0)};
+            const int hi_yz[2] = {min(my_y0 + 1, lgl.H - 1), min(my_z0 + 1, lgl.Z - 1)};
 #pragma unroll
-            for (int a = 0; a < DIM; ++a) {
-                atomicMax(&dd.bbox[my_level][a], ~static_cast<uint32_t>(max(cell[a], 0)));
-                atomicMax(&dd.bbox[my_level][3 + a], static_cast<uint32_t>(min(cell[a] + 1, ext[a] - 1)));
+            for (int side = 0; side < 2; ++side) {
+                const int lo = side ? max(xa, half) : xa;
+                const int hi = side ? xb : min(xb, half - 1);
+                if (lo <= hi) {
+                    uint32_t* bb = dd.bbox[2 * my_level + side];
+                    atomicMax(&bb[0], ~static_cast<uint32_t>(lo));
+                    atomicMax(&bb[3], static_cast<uint32_t>(hi));
+#pragma unroll
+                    for (int a = 1; a < DIM; ++a) {
+                        atomicMax(&bb[a], ~static_cast<uint32_t>(lo_yz[a - 1]));
+                        atomicMax(&bb[3 + a], static_cast<uint32_t>(hi_yz[a - 1]));
+                    }
+                }
             }
         }
         __syncthreads();
-        if (tid < p.L) {
+        const int nw = 2 * p.L;
+        if (tid < nw) {
             const bool any = dd.bbox[tid][0] != 0u;
             int lo[3] = {0, 0, 0}, ext[3] = {1, 1, 1};
 #pragma unroll
@@ -436,13 +457,13 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
             dd.any_direct = 0;
         }
         __syncthreads();
-        if (tid < p.L) {
-            // windows in ascending size (ties by level) while the total fits
-            // the table; the total only grows, so a level that does not fit
+        if (tid < nw) {
+            // windows in ascending size (ties by index) while the total fits
+            // the table; the total only grows, so a window that does not fit
             // excludes every larger one
             const int mine_rows = dd.rows[tid];
             int before = 0;
-            for (int k = 0; k < p.L; ++k) {
+            for (int k = 0; k < nw; ++k) {
                 const int r = dd.rows[k];
                 if (r < mine_rows || (r == mine_rows && k < tid)) before += r;
             }
@@ -452,13 +473,32 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
             if (!fits && mine_rows > 0) atomicOr(&dd.any_direct, 1);
         }
         __syncthreads();
+
+        // D2: each windowed corner takes a place in its pixel's list (LDS
+        // integer atomics; counts stay below 2^16, at most WAVES * 64 * NC
+        // entries) and leaves phase C (its offset in the slot is cleared)
+#pragma unroll
+        for (int k = 0; k < NC; ++k) {
+            slot_id[k] = 0xffffffffu;
+            pos[k] = 0u;
+            const int cx = k & 1, cy = (k >> 1) & 1, cz = k >> 2;
+            const int x = my_x0 + cx;
+            const int w = 2 * my_level + (x >= half ? 1 : 0);
+            if (my_in && mine.off[k] != kOutOfRange && dd.base[w] >= 0) {
+                const int lx = x - dd.ox[w], ly = my_y0 + cy - dd.oy[w], lz = my_z0 + cz - dd.oz[w];
+                slot_id[k] = static_cast<uint32_t>(dd.base[w] + (lz * dd.hh[w] + ly) * dd.ww[w] + lx);
+                const uint32_t sh = (slot_id[k] & 1u) * 16u;
+                pos[k] = (atomicAdd(&dd.count2[slot_id[k] >> 1], 1u << sh) >> sh) & 0xffffu;
+                slots[wave][lane].off[k] = kOutOfRange;
+            }
+        }
     }
 
     // ---- Phase C: grad_value[row_c][d] += A * w_c * g[t][d] over the flat
     // index (slot, corner, channel padded to R); 64 / R rows per instruction
     // (R <= 64), or a row in R / 64 instructions.  NG * R >= 128, so the trip
-    // count is the same on every lane.  With DEDUP only levels without a
-    // window take this path.
+    // count is the same on every lane.  With DEDUP only the corners outside
+    // every window are left here.
     wave_lds_sync();
     constexpr int kLog2NC = DIM == 2 ? 2 : 3;
     const uint32_t log2R = bp.log2R;
@@ -475,14 +515,7 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
         const BwdSlot<NC, DIM>* sp = &slots[wave][sig];
         const uint32_t off = sp->off[k];
         const float a = sp->a;
-        bool direct = true;
-        if constexpr (DEDUP) {
-            const int gs = static_cast<int>(sig & (NG - 1));
-            const int ss = static_cast<int>(sig / NG) * G + (gs & (G - 1));
-            const int ls = static_cast<int>(fast_div(static_cast<uint32_t>(min(ss, p.LP - 1)), p.div_P));
-            direct = dd.base[ls] < 0;
-        }
-        if (direct && d < static_cast<uint32_t>(D) && off != kOutOfRange && a != 0.0f) {
+        if (d < static_cast<uint32_t>(D) && off != kOutOfRange && a != 0.0f) {
             const int ts = static_cast<int>(sig & (NG - 1)) >> log2G;
             const float gd = gtile[ts * D + static_cast<int>(d)];
             __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(a * sp->w[k] * gd, rgv, off + 4u * d,
@@ -490,33 +523,25 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
         }
     }
 
-    // ---- Phase D (de-duplication).  D2: each contribution of a windowed
-    // level takes a place in its pixel's list (LDS integer atomics); D3:
-    // exclusive prefix sum of the counts; D4: entries (A*w, tile row) are
-    // written to the lists, over the slot array, which is no longer read;
-    // D5: groups of R lanes sum each pixel's list, channel per lane, and add
-    // the row to grad_value with one coalesced atomic per channel.
+    // ---- Phase D (de-duplication), after D2 above.  D3: exclusive prefix
+    // sum of the counts; D4: entries (A*w, tile row) are written to the
+    // lists, over the slot array, which is no longer read; D5: groups of R
+    // lanes sum each pixel's list, channel per lane, and add the row to
+    // grad_value with one coalesced atomic per channel.
     if constexpr (DEDUP) {
-        uint32_t slot_id[NC], pos[NC];
-#pragma unroll
-        for (int k = 0; k < NC; ++k) {
-            slot_id[k] = 0xffffffffu;
-            pos[k] = 0u;
-            const int cx = k & 1, cy = (k >> 1) & 1, cz = k >> 2;
-            const int base = dd.base[my_level];
-            if (my_in && base >= 0 && mine.off[k] != kOutOfRange) {
-                const int x = my_x0 + cx - dd.ox[my_level];
-                const int y = my_y0 + cy - dd.oy[my_level];
-                const int z = my_z0 + cz - dd.oz[my_level];
-                slot_id[k] = static_cast<uint32_t>(base + (z * dd.hh[my_level] + y) * dd.ww[my_level] + x);
-                // counts stay below 2^16 (at most WAVES * 64 * NC entries)
-                const uint32_t sh = (slot_id[k] & 1u) * 16u;
-                pos[k] = (atomicAdd(&dd.count2[slot_id[k] >> 1], 1u << sh) >> sh) & 0xffffu;
-            }
-        }
         __syncthreads();
-        // D3: exclusive scan of count[0, nslots) into offs (4 slots per thread)
+        // D3: exclusive scans of count[0, nslots) into offs and of the
+        // non-empty slots into a compact list, ascending, of (list start << 16
+        // | slot) behind the entry lists in the slot array (4 slots per
+        // thread; both scans in one, packed as sum << 16 | non-empty, no
+        // carry below 2^16).  A non-empty slot's entries end where the next
+        // one's start: empty slots own none.  D5 walks the compact list in 3D,
+        // whose voxel windows are mostly empty (measured faster there); in 2D
+        // it walks every window slot (measured faster than the compaction).
+        constexpr bool kCompact = DIM == 3;
         const int nslots = dd.nslots;
+        DedupEntry* list = reinterpret_cast<DedupEntry*>(&slots[0][0]);
+        uint32_t* nzlist = reinterpret_cast<uint32_t*>(list + WAVES * kWave * NC);
         {
             const int i0 = 4 * tid;
             uint32_t cv[4];
@@ -525,8 +550,10 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
                 const uint32_t w2 = i0 < kDedupSlots ? dd.count2[(i0 >> 1) + (e >> 1)] : 0u;
                 cv[e] = i0 + e < nslots ? (w2 >> ((e & 1) * 16)) & 0xffffu : 0u;
             }
-            const uint32_t mine_sum = cv[0] + cv[1] + cv[2] + cv[3];
-            uint32_t incl = mine_sum;
+            uint32_t mine_pk = 0u;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) mine_pk += (cv[e] << 16) | (cv[e] != 0u ? 1u : 0u);
+            uint32_t incl = mine_pk;
 #pragma unroll
             for (int b = 1; b < kWave; b <<= 1) {
                 const uint32_t o = static_cast<uint32_t>(__shfl_up(static_cast<int>(incl), b, kWave));
@@ -536,20 +563,44 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
             __syncthreads();
             uint32_t before = 0u;
             for (int w = 0; w < wave; ++w) before += dd.wave_sum[w];
-            uint32_t run = before + incl - mine_sum;
+            uint32_t run = before + incl - mine_pk;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                if (i0 + e < nslots) dd.offs[i0 + e] = static_cast<uint16_t>(run);
-                run += cv[e];
+                if (i0 + e < nslots) dd.offs[i0 + e] = static_cast<uint16_t>(run >> 16);
+                if (kCompact && cv[e] != 0u)
+                    nzlist[run & 0xffffu] = (run & 0xffff0000u) | static_cast<uint32_t>(i0 + e);
+                run += (cv[e] << 16) | (cv[e] != 0u ? 1u : 0u);
             }
             if (tid == kThreads - 1) {
                 uint32_t all = 0u;
                 for (int w = 0; w < WAVES; ++w) all += dd.wave_sum[w];
-                dd.offs[nslots] = static_cast<uint16_t>(all);
+                dd.offs[nslots] = static_cast<uint16_t>(all >> 16);
+                if (kCompact) {
+                    dd.nnz = static_cast<int>(all & 0xffffu);
+                    nzlist[all & 0xffffu] = all & 0xffff0000u;   // end of the last list
+                }
             }
         }
         __syncthreads();
-        DedupEntry* list = reinterpret_cast<DedupEntry*>(&slots[0][0]);
+        // each window's part of the compact list (binary search: the list is
+        // ascending and a window's slots are one range)
+        if (kCompact && tid < 2 * p.L && dd.base[tid] >= 0) {
+            const int nnz = dd.nnz;
+            int bounds[2];
+            const int key[2] = {dd.base[tid], dd.base[tid] + dd.rows[tid]};
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                int lo = 0, hi = nnz;
+                while (lo < hi) {
+                    const int mid = (lo + hi) >> 1;
+                    if (static_cast<int>(nzlist[mid] & 0xffffu) < key[h]) lo = mid + 1;
+                    else hi = mid;
+                }
+                bounds[h] = lo;
+            }
+            dd.nz_begin[tid] = bounds[0];
+            dd.nz_end[tid] = bounds[1];
+        }
 #pragma unroll
         for (int k = 0; k < NC; ++k) {
             if (slot_id[k] != 0xffffffffu) {
@@ -560,23 +611,35 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
             }
         }
         __syncthreads();
-        // D5: level by level, groups of R lanes take every ngroups-th pixel
+        // D5: window by window, groups of R lanes take every ngroups-th pixel
+        // (non-empty pixel in 3D)
         const int rl = 1 << log2R;               // lanes per row (D <= 64)
         const int ngroups = kThreads / rl;
         const int grp = tid / rl, ch = tid % rl;
         // lanes past D (D not a power of two) read channel D-1 and never store
         const uint32_t chc = static_cast<uint32_t>(min(ch, D - 1));
         const float* gflat = gtile_all;
-        for (int l = 0; l < p.L; ++l) {
-            const int base = dd.base[l];
+        for (int w = 0; w < 2 * p.L; ++w) {
+            const int base = dd.base[w];
             if (base < 0) continue;
-            const int rows = dd.rows[l];
-            const int ww = dd.ww[l], hh = dd.hh[l], ox = dd.ox[l], oy = dd.oy[l], oz = dd.oz[l];
-            const float rw = dd.rcp_ww[l], rh = dd.rcp_hh[l];
-            const LevelGeom lg = smeta[l * p.P];
-            for (int local = grp; local < rows; local += ngroups) {
-                const uint32_t b0 = dd.offs[base + local], b1 = dd.offs[base + local + 1];
-                if (b0 == b1) continue;
+            const int ww = dd.ww[w], hh = dd.hh[w], ox = dd.ox[w], oy = dd.oy[w], oz = dd.oz[w];
+            const float rw = dd.rcp_ww[w], rh = dd.rcp_hh[w];
+            const LevelGeom lg = smeta[(w >> 1) * p.P];
+            const int i_end = kCompact ? dd.nz_end[w] : dd.rows[w];
+            for (int idx = (kCompact ? dd.nz_begin[w] : 0) + grp; idx < i_end; idx += ngroups) {
+                int local;
+                uint32_t b0, b1;
+                if constexpr (kCompact) {
+                    const uint32_t here = nzlist[idx], next = nzlist[idx + 1];
+                    local = static_cast<int>(here & 0xffffu) - base;
+                    b0 = here >> 16;
+                    b1 = next >> 16;
+                } else {
+                    local = idx;
+                    b0 = dd.offs[base + idx];
+                    b1 = dd.offs[base + idx + 1];
+                    if (b0 == b1) continue;
+                }
                 // four entries per round: their eight LDS reads overlap
                 float acc0 = 0.0f, acc1 = 0.0f;
                 uint32_t e = b0;
