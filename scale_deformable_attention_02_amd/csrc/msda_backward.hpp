@@ -151,7 +151,7 @@ __device__ __forceinline__ void load_grad(__amdgpu_buffer_rsrc_t r, uint32_t off
 // sized so that two workgroups share a CU's LDS; 3D (one workgroup per CU,
 // larger slots): the finer levels' voxel boxes need more.
 template <int DIM>
-constexpr int dedup_slots() { return DIM == 2 ? 3072 : 4096; }
+constexpr int dedup_slots() { return DIM == 2 ? 3072 : 8192; }
 
 // floor(x / d) for x < 2^24, d >= 1, from rcp = 1.0f / d: x * rcp is within
 // one of x / d (both exact below 2^24, rcp within 2^-24 relative), so one
@@ -173,6 +173,7 @@ struct DedupShared {
     float rcp_ww[2 * kMaxLevels], rcp_hh[2 * kMaxLevels];
     int nslots;
     int nnz;                        // non-empty slots
+    uint32_t total;                 // entries
     int nz_begin[2 * kMaxLevels], nz_end[2 * kMaxLevels];   // window's part of the compact list
     int any_direct;                 // some corners take the direct atomics of phase C
     uint32_t wave_sum[16];
@@ -233,10 +234,11 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
     constexpr int VEC = ValueTraits<TV>::kVec;
     constexpr int kThreads = WAVES * kWave;
     constexpr int kDedupSlots = dedup_slots<DIM>();
-    static_assert(!DEDUP || 4 * kThreads >= kDedupSlots,
-                  "de-duplication: four table slots per thread at most");
+    // D3 scans an even number of table slots per thread
+    constexpr int kSpt = ((kDedupSlots + kThreads - 1) / kThreads + 1) & ~1;
+    static_assert(!DEDUP || kSpt * kThreads >= kDedupSlots, "de-duplication: scan covers the table");
     static_assert(!DEDUP || sizeof(BwdSlot<NC, DIM>) * WAVES * kWave >=
-                                NC * sizeof(DedupEntry) * WAVES * kWave + 4 * (kDedupSlots + 1),
+                                NC * sizeof(DedupEntry) * WAVES * kWave + 4 * kDedupSlots,
                   "de-duplication: the entry lists and the compact slot list reuse the slot array");
     const Params& p = bp.f;
 
@@ -532,7 +534,7 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
         __syncthreads();
         // D3: exclusive scans of count[0, nslots) into offs and of the
         // non-empty slots into a compact list, ascending, of (list start << 16
-        // | slot) behind the entry lists in the slot array (4 slots per
+        // | slot) behind the entry lists in the slot array (kSpt slots per
         // thread; both scans in one, packed as sum << 16 | non-empty, no
         // carry below 2^16).  A non-empty slot's entries end where the next
         // one's start: empty slots own none.  D5 walks the compact list in 3D,
@@ -543,16 +545,16 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
         DedupEntry* list = reinterpret_cast<DedupEntry*>(&slots[0][0]);
         uint32_t* nzlist = reinterpret_cast<uint32_t*>(list + WAVES * kWave * NC);
         {
-            const int i0 = 4 * tid;
-            uint32_t cv[4];
+            const int i0 = kSpt * tid;
+            uint32_t cv[kSpt];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t w2 = i0 < kDedupSlots ? dd.count2[(i0 >> 1) + (e >> 1)] : 0u;
+            for (int e = 0; e < kSpt; ++e) {
+                const uint32_t w2 = i0 + e < kDedupSlots ? dd.count2[(i0 + e) >> 1] : 0u;
                 cv[e] = i0 + e < nslots ? (w2 >> ((e & 1) * 16)) & 0xffffu : 0u;
             }
             uint32_t mine_pk = 0u;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) mine_pk += (cv[e] << 16) | (cv[e] != 0u ? 1u : 0u);
+            for (int e = 0; e < kSpt; ++e) mine_pk += (cv[e] << 16) | (cv[e] != 0u ? 1u : 0u);
             uint32_t incl = mine_pk;
 #pragma unroll
             for (int b = 1; b < kWave; b <<= 1) {
@@ -565,7 +567,7 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
             for (int w = 0; w < wave; ++w) before += dd.wave_sum[w];
             uint32_t run = before + incl - mine_pk;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
+            for (int e = 0; e < kSpt; ++e) {
                 if (i0 + e < nslots) dd.offs[i0 + e] = static_cast<uint16_t>(run >> 16);
                 if (kCompact && cv[e] != 0u)
                     nzlist[run & 0xffffu] = (run & 0xffff0000u) | static_cast<uint32_t>(i0 + e);
@@ -575,10 +577,8 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
                 uint32_t all = 0u;
                 for (int w = 0; w < WAVES; ++w) all += dd.wave_sum[w];
                 dd.offs[nslots] = static_cast<uint16_t>(all >> 16);
-                if (kCompact) {
-                    dd.nnz = static_cast<int>(all & 0xffffu);
-                    nzlist[all & 0xffffu] = all & 0xffff0000u;   // end of the last list
-                }
+                dd.nnz = static_cast<int>(all & 0xffffu);
+                dd.total = all >> 16;   // end of the last list
             }
         }
         __syncthreads();
@@ -619,6 +619,8 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
         // lanes past D (D not a power of two) read channel D-1 and never store
         const uint32_t chc = static_cast<uint32_t>(min(ch, D - 1));
         const float* gflat = gtile_all;
+        const int nnz_all = dd.nnz;
+        const uint32_t total_all = dd.total;
         for (int w = 0; w < 2 * p.L; ++w) {
             const int base = dd.base[w];
             if (base < 0) continue;
@@ -630,10 +632,10 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
                 int local;
                 uint32_t b0, b1;
                 if constexpr (kCompact) {
-                    const uint32_t here = nzlist[idx], next = nzlist[idx + 1];
+                    const uint32_t here = nzlist[idx];
                     local = static_cast<int>(here & 0xffffu) - base;
                     b0 = here >> 16;
-                    b1 = next >> 16;
+                    b1 = idx + 1 < nnz_all ? nzlist[idx + 1] >> 16 : total_all;
                 } else {
                     local = idx;
                     b0 = dd.offs[base + idx];
