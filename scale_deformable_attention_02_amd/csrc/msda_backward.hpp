@@ -22,7 +22,10 @@
 // with fp32 buffer atomics, lanes mapped to consecutive channels of a row so
 // that one instruction updates whole 64-byte sectors: the L2 retires about one
 // atomic request per sector, whatever the number of dwords in it, so a layout
-// with 8 dwords per 128-byte row per instruction runs 4x slower.
+// with 8 dwords per 128-byte row per instruction runs 4x slower.  Large
+// launches run de-duplicating workgroups instead (phases D1-D5 below): the
+// contributions of a workgroup's samples to each grad_value row are summed in
+// LDS-fed registers first, and the row gets one atomic update.
 #pragma once
 
 #include <type_traits>
@@ -47,8 +50,8 @@ struct BwdParams {
 
 // Output-gradient rows of one wave's tiles in LDS: T * D floats, at most
 // T * CPL * 16 bytes of value channels (256 floats for fp32 values, 512 for
-// bf16).  The 3D de-duplicating kernel, whose slots are larger, holds 256 per
-// wave; its launches need T * D <= 256.
+// bf16).  The de-duplicating kernels hold 256 per wave (their LDS budget);
+// their launches need T * D <= 256.
 template <int DIM, bool DEDUP>
 constexpr int grad_tile_floats() { return DEDUP ? 256 : 512; }
 
@@ -219,8 +222,8 @@ static_assert(bwd_dedup_lds<2, 16>() + 512 <= 80 * 1024,
               "two 2D de-duplicating workgroups of 16 waves share a CU's 160 KB of LDS");
 static_assert(bwd_dedup_lds<3, 16>() + 512 <= 160 * 1024,
               "a 3D de-duplicating workgroup of 16 waves fits the LDS");
-static_assert(16 * kWave * 8 < 65536 && dedup_slots<2>() % 4 == 0 && dedup_slots<3>() % 4 == 0,
-              "16-bit counts and list offsets; four table slots per scan thread");
+static_assert(16 * kWave * 8 < 65536 && dedup_slots<2>() % 2 == 0 && dedup_slots<3>() % 2 == 0,
+              "16-bit counts and list offsets, counts packed in pairs");
 
 // WAVES waves per workgroup.  DEDUP (D <= 64, WAVES consecutive waves of one
 // (image, head) slice): contributions to grad_value rows that several samples
