@@ -40,4 +40,7 @@ STAGED = [
     # bf16, 64 channels, L*P = 8: the backward's de-duplicating workgroups
     # would not fit the LDS (8 tiles per wave), so it takes the direct path
     (3, "bf16", 1, ((16, 16, 16), (8, 8, 8)), 8300, 8, 64, 4, "random_refs"),
+    # a level one pixel wide (the backward's x < W/2 window is empty) and an
+    # odd width
+    (2, "f32", 1, ((97, 1), (13, 3)), 16500, 4, 16, 4, "random_refs"),
 ]
