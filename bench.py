@@ -337,9 +337,9 @@ def main(argv=None):
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
-              "the core needs no communication, see the sharding notes in DESIGN.md",
-              file=sys.stderr)
+        print(f"bench.py: measures one GPU only (--gpus {args.gpus} requested); the core "
+              "needs no communication between GPUs: shard by image, query or head and run "
+              "one process per GPU", file=sys.stderr)
         return 2
 
     import torch

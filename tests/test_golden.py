@@ -19,7 +19,7 @@ def test_dense_attention_counts_and_sampled_point_unit():
         assert tokens == row["tokens"]
         # the printed figure is tokens^2 rounded to three significant digits
         assert tokens ** 2 == pytest.approx(row["entries_approx"], rel=3e-3)
-    # the unit this build reports: one sampled point per (n, q, m, l, p);
+    # the throughput unit: one sampled point per (n, q, m, l, p);
     # per head a query reads L x P samples, N x L x P across N queries
     w = CONFIGS["detr_encoder"]
     assert w.sampled_points == w.N * w.queries_per_image * w.M * w.L * w.P
