@@ -42,10 +42,9 @@ typedef uint32_t v2u __attribute__((ext_vector_type(2)));
 constexpr int kBM = 128, kBN = 128, kBK = 32;
 constexpr int kThreads = 256;
 
-// LDS row strides in bytes, padded by 16 B so that the 8 lanes of a b128
-// read phase start on distinct 4-bank groups.
-template <typename T>
-constexpr int row_stride() { return kBK * static_cast<int>(sizeof(T)) + 16; }
+// fp32 kernel: LDS row stride in bytes, padded by 16 B so that the 8 lanes of
+// a b128 read phase start on distinct 4-bank groups.
+constexpr int kF32Stride = kBK * 4 + 16;
 
 struct LinearParams {
     const void* x;         // this launch's rows
@@ -58,42 +57,9 @@ struct LinearParams {
     uint32_t num_blocks;
 };
 
-template <typename T>
-struct Tile;
-
-// bf16: a tile row of 32 values is 64 B = 4 chunks of 16 B; 128 rows = 512
-// chunks, 2 per thread.
-template <>
-struct Tile<msda::Bf16> {
-    static constexpr int kChunks = 2;
-    __device__ static void load(__amdgpu_buffer_rsrc_t r, uint32_t row0, uint32_t rows_valid,
-                                uint32_t k0, uint32_t K, int tid, uint32_t (&buf)[kChunks][4]) {
-#pragma unroll
-        for (int i = 0; i < kChunks; ++i) {
-            const int c = tid + i * kThreads;
-            const uint32_t row = static_cast<uint32_t>(c >> 2), col = static_cast<uint32_t>(c & 3);
-            const uint32_t off = row < rows_valid ? ((row0 + row) * K + k0 + col * 8u) * 2u
-                                                  : msda::kOutOfRange;
-            const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-            buf[i][0] = v[0];
-            buf[i][1] = v[1];
-            buf[i][2] = v[2];
-            buf[i][3] = v[3];
-        }
-    }
-    __device__ static void store(unsigned char* lds, int tid, const uint32_t (&buf)[kChunks][4]) {
-#pragma unroll
-        for (int i = 0; i < kChunks; ++i) {
-            const int c = tid + i * kThreads;
-            *reinterpret_cast<uint4*>(lds + (c >> 2) * row_stride<msda::Bf16>() + (c & 3) * 16) =
-                make_uint4(buf[i][0], buf[i][1], buf[i][2], buf[i][3]);
-        }
-    }
-};
-
-// fp32: a tile row of 32 values is 128 B = 8 chunks; 1024 chunks, 4 per thread.
-template <>
-struct Tile<float> {
+// fp32 kernel: one K step of a 128-row tile, 32 values = 128 B = 8 chunks of
+// 16 B per row; 1024 chunks, 4 per thread, global -> registers -> LDS.
+struct F32Tile {
     static constexpr int kChunks = 4;
     __device__ static void load(__amdgpu_buffer_rsrc_t r, uint32_t row0, uint32_t rows_valid,
                                 uint32_t k0, uint32_t K, int tid, uint32_t (&buf)[kChunks][4]) {
@@ -114,57 +80,39 @@ struct Tile<float> {
 #pragma unroll
         for (int i = 0; i < kChunks; ++i) {
             const int c = tid + i * kThreads;
-            *reinterpret_cast<uint4*>(lds + (c >> 3) * row_stride<float>() + (c & 7) * 16) =
+            *reinterpret_cast<uint4*>(lds + (c >> 3) * kF32Stride + (c & 7) * 16) =
                 make_uint4(buf[i][0], buf[i][1], buf[i][2], buf[i][3]);
         }
     }
 };
 
-// One K step (32) of a wave's 2 x 2 tiles: A rows am..am+63, B rows bn..bn+63.
-template <typename T>
-__device__ __forceinline__ void mma_step(const unsigned char* la, const unsigned char* lb,
-                                         int am, int bn, int lane, f32x16_t (&acc)[2][2]) {
+// fp32 kernel: one K step (32) of a wave's 2 x 2 tiles, A rows am..am+63, B
+// rows bn..bn+63.  Lane half h takes k = 16 h + kk of the step: 16
+// consecutive floats.
+__device__ __forceinline__ void mma_step_f32(const unsigned char* la, const unsigned char* lb,
+                                             int am, int bn, int lane, f32x16_t (&acc)[2][2]) {
     const int r = lane & 31, h = lane >> 5;
-    if constexpr (sizeof(T) == 2) {
-        constexpr int S = row_stride<msda::Bf16>();
+    constexpr int S = kF32Stride;
+    float4 a[2][4], b[2][4];
 #pragma unroll
-        for (int kk = 0; kk < kBK / 16; ++kk) {
-            bf16x8_t a[2], b[2];
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                a[t] = *reinterpret_cast<const bf16x8_t*>(la + (am + 32 * t + r) * S + (kk * 16 + h * 8) * 2);
-                b[t] = *reinterpret_cast<const bf16x8_t*>(lb + (bn + 32 * t + r) * S + (kk * 16 + h * 8) * 2);
-            }
+        for (int v = 0; v < 4; ++v) {
+            a[t][v] = *reinterpret_cast<const float4*>(la + (am + 32 * t + r) * S + (h * 16 + v * 4) * 4);
+            b[t][v] = *reinterpret_cast<const float4*>(lb + (bn + 32 * t + r) * S + (h * 16 + v * 4) * 4);
+        }
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
-        }
-    } else {
-        // lane half h takes k = 16 h + kk of the step: 16 consecutive floats
-        constexpr int S = row_stride<float>();
-        float4 a[2][4], b[2][4];
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                a[t][v] = *reinterpret_cast<const float4*>(la + (am + 32 * t + r) * S + (h * 16 + v * 4) * 4);
-                b[t][v] = *reinterpret_cast<const float4*>(lb + (bn + 32 * t + r) * S + (h * 16 + v * 4) * 4);
-            }
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        const float av = e == 0 ? a[i][v].x : e == 1 ? a[i][v].y : e == 2 ? a[i][v].z : a[i][v].w;
-                        const float bv = e == 0 ? b[j][v].x : e == 1 ? b[j][v].y : e == 2 ? b[j][v].z : b[j][v].w;
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(bv, av, acc[i][j], 0, 0, 0);
-                    }
-    }
+                for (int j = 0; j < 2; ++j) {
+                    const float av = e == 0 ? a[i][v].x : e == 1 ? a[i][v].y : e == 2 ? a[i][v].z : a[i][v].w;
+                    const float bv = e == 0 ? b[j][v].x : e == 1 ? b[j][v].y : e == 2 ? b[j][v].z : b[j][v].w;
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(bv, av, acc[i][j], 0, 0, 0);
+                }
 }
 
 template <typename TY>
@@ -428,10 +376,10 @@ __global__ __launch_bounds__(kThreads) void linear_bf16_kernel(LinearParams p) {
     store_tiles<TY>(p, row0, col0, am, bn, lane, acc);
 }
 
-template <typename TX, typename TY>
-__global__ __launch_bounds__(kThreads) void linear_kernel(LinearParams p) {
-    constexpr int S = row_stride<TX>();
-    constexpr int kTileBytes = 128 * S;
+// fp32 operands: register-staged, double-buffered LDS.
+template <typename TY>
+__global__ __launch_bounds__(kThreads) void linear_f32_kernel(LinearParams p) {
+    constexpr int kTileBytes = 128 * kF32Stride;
     __shared__ __align__(16) unsigned char lds[2][2][kTileBytes];   // [stage][X, W]
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -450,11 +398,11 @@ __global__ __launch_bounds__(kThreads) void linear_kernel(LinearParams p) {
     f32x16_t acc[2][2];
     init_with_bias(p, col0, bn, lane, acc);
 
-    uint32_t bx[Tile<TX>::kChunks][4], bw[Tile<TX>::kChunks][4];
-    Tile<TX>::load(rx, row0, rows_x, 0, K, tid, bx);
-    Tile<TX>::load(rw, col0, rows_w, 0, K, tid, bw);
-    Tile<TX>::store(lds[0][0], tid, bx);
-    Tile<TX>::store(lds[0][1], tid, bw);
+    uint32_t bx[F32Tile::kChunks][4], bw[F32Tile::kChunks][4];
+    F32Tile::load(rx, row0, rows_x, 0, K, tid, bx);
+    F32Tile::load(rw, col0, rows_w, 0, K, tid, bw);
+    F32Tile::store(lds[0][0], tid, bx);
+    F32Tile::store(lds[0][1], tid, bw);
     __syncthreads();
 
     const int steps = p.K / kBK;
@@ -462,13 +410,13 @@ __global__ __launch_bounds__(kThreads) void linear_kernel(LinearParams p) {
         const int cur = s & 1;
         const bool more = s + 1 < steps;
         if (more) {
-            Tile<TX>::load(rx, row0, rows_x, (s + 1) * kBK, K, tid, bx);
-            Tile<TX>::load(rw, col0, rows_w, (s + 1) * kBK, K, tid, bw);
+            F32Tile::load(rx, row0, rows_x, (s + 1) * kBK, K, tid, bx);
+            F32Tile::load(rw, col0, rows_w, (s + 1) * kBK, K, tid, bw);
         }
-        mma_step<TX>(lds[cur][0], lds[cur][1], am, bn, lane, acc);
+        mma_step_f32(lds[cur][0], lds[cur][1], am, bn, lane, acc);
         if (more) {
-            Tile<TX>::store(lds[cur ^ 1][0], tid, bx);
-            Tile<TX>::store(lds[cur ^ 1][1], tid, bw);
+            F32Tile::store(lds[cur ^ 1][0], tid, bx);
+            F32Tile::store(lds[cur ^ 1][1], tid, bw);
         }
         __syncthreads();
     }
@@ -483,7 +431,7 @@ void launch_linear(const LinearParams& p, hipStream_t s) {
         hipLaunchKernelGGL((linear_bf16_kernel<TY, kBf16Step, kBf16Stages>), dim3(p.num_blocks),
                            dim3(kThreads), 0, s, p);
     else
-        hipLaunchKernelGGL((linear_kernel<TX, TY>), dim3(p.num_blocks), dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL((linear_f32_kernel<TY>), dim3(p.num_blocks), dim3(kThreads), 0, s, p);
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
