@@ -31,6 +31,9 @@
 
 namespace {
 
+// Waves that fill the GPU: 256 CUs x 4 SIMDs x 4 waves.
+constexpr int64_t kFillWaves = 4096;
+
 using msda::FastDiv;
 using msda::Params;
 using msda::StagedParams;
@@ -144,9 +147,7 @@ int forward(const void* value, int value_dtype, const int64_t* spatial_shapes,
     const int cpl = 1 << ceil_log2(nchunk);
     const int ng = msda::kWave / cpl;
     const int tiles_fit = 1 << floor_log2(msda::kWave / LP);
-    const int T = tiles_fit < ng ? tiles_fit : ng;
-    const int G = ng / T;
-    const int NI = static_cast<int>((LP + G - 1) / G);
+    const int t_max = tiles_fit < ng ? tiles_fit : ng;
 
     // Work per launch: whole images while the value slice, the locations and
     // the tile count stay below 2^31 bytes / 2^30 tiles (32-bit buffer
@@ -174,6 +175,13 @@ int forward(const void* value, int value_dtype, const int64_t* spatial_shapes,
         const int64_t nbatch = (N - n0 < nb) ? N - n0 : nb;
         for (int64_t q0 = 0; q0 < Lq; q0 += nq) {
             const int64_t nquery = (Lq - q0 < nq) ? Lq - q0 : nq;
+            // Small launches are latency-bound: fewer tiles per wave (more
+            // point groups per tile) until the waves can fill the GPU.
+            const int64_t tiles = nbatch * M * nquery;
+            int T = t_max;
+            while (T > 1 && tiles < int64_t{kFillWaves} * T) T >>= 1;
+            const int G = ng / T;
+            const int NI = static_cast<int>((LP + G - 1) / G);
             const int64_t waves_per_slice = (nquery + T - 1) / T;
             const int64_t waves = nbatch * M * waves_per_slice;
             const int64_t first_row = (n0 * Lq + q0) * M;
@@ -220,7 +228,6 @@ int forward(const void* value, int value_dtype, const int64_t* spatial_shapes,
             // queries between them.  (3D pyramids' coarsest level is rarely
             // small enough to copy whole: 8^3 voxels of 32 fp32 channels are
             // 64 KB; there the direct kernel is faster.)
-            const int64_t tiles = nbatch * M * nquery;
             if (DIM == 2 && P % G == 0 && tiles >= MSDA_STAGED_MIN_TILES) {
                 const int64_t pass = int64_t{msda::kStagedWaves} * T;
                 const int64_t slices = nbatch * M;

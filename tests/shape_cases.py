@@ -6,7 +6,8 @@ bf16 value, 2D and 3D, batch > 1, Lq a multiple of no tile count).
 
 STAGED: launches of >= 65536 (query, head) tiles: levels that fit the LDS
 budget of the staged forward kernel or not, fp32/bf16, D from 4 to 64
-channels, 2D/3D, query counts that leave ragged workgroups and waves.
+channels, 2D/3D, query counts that leave ragged workgroups and waves, and a 2D
+launch that the direct kernel takes with several tiles per wave.
 """
 
 SMALL = [
@@ -43,4 +44,8 @@ STAGED = [
     # a level one pixel wide (the backward's x < W/2 window is empty) and an
     # odd width
     (2, "f32", 1, ((97, 1), (13, 3)), 16500, 4, 16, 4, "random_refs"),
+    # L * P = 9, P = 3: four tiles and two point groups per wave, G does not
+    # divide P, so the forward takes the direct kernel with several tiles per
+    # wave
+    (2, "f32", 1, ((60, 90), (30, 45), (15, 23)), 9000, 8, 32, 3, "random_refs"),
 ]
