@@ -455,10 +455,11 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Probability-aware pruning: lanes i*NG + g (i = 0, 1, ...) hold the samples
-// of point group g.  Kept samples are packed, in order, to the front of their
-// group's list, so phase B runs max-over-groups iterations instead of NI.
-// Lane masks of one group: bits g, g + NG, g + 2 NG, ...
+// Probability-aware pruning in the direct kernel: lanes i*NG + g (i = 0, 1,
+// ...) hold the samples of point group g.  Kept samples are packed, in order,
+// to the front of their group's list, so phase B runs max-over-groups
+// iterations instead of NI (the staged kernel gives dropped samples dead slots
+// instead).  Lane masks of one group: bits g, g + NG, g + 2 NG, ...
 template <int NG>
 __device__ __forceinline__ uint64_t group_lanes(int g) {
     constexpr uint64_t rep = NG >= 64 ? 1ull : ~0ull / ((1ull << NG) - 1ull);
@@ -613,12 +614,8 @@ struct StagedParams {
 };
 
 // Two 16-wave workgroups per CU need 8 waves per SIMD, i.e. at most 64 VGPRs.
-// Every variant is held to that except the pruned one on bf16 values, which
-// would spill 40 bytes per lane there and measured slower than one workgroup
-// per CU (the fp32 pruned variant spills 20 bytes and gains).
 template <typename TV, typename TO, int DIM, int CPL, bool FUSED = false, bool PRUNE = false>
-__global__ __launch_bounds__(kStagedThreads)
-__attribute__((amdgpu_waves_per_eu(PRUNE && sizeof(TV) == 2 ? 1 : 8)))
+__global__ __launch_bounds__(kStagedThreads) __attribute__((amdgpu_waves_per_eu(8)))
 void msda_forward_staged_kernel(StagedParams sp) {
     constexpr int NC = DIM == 2 ? 4 : 8;
     constexpr int NG = kWave / CPL;
@@ -759,22 +756,15 @@ void msda_forward_staged_kernel(StagedParams sp) {
         // ---- Phase A
         if constexpr (FUSED) finish_sample_fused<DIM, ilog2<NG>()>(live, p.log2G, xyz, a, ref);
         const Slot<NC> sl = make_slot<DIM>(xyz, a, live, lga, slot_base, slot_stride, slot_invalid);
-        int hbm_end = ni_hbm, lds_end = NI;
+        const int hbm_end = ni_hbm, lds_end = NI;
         if constexpr (PRUNE) {
-            // pack kept samples within each segment (HBM levels, then LDS levels)
+            // a dropped sample keeps its place with a dead slot: its loads
+            // are out of range (HBM levels) or hit the zero row (LDS levels),
+            // which costs no memory traffic; measured faster here than
+            // packing the kept samples, which needs more registers than two
+            // workgroups per CU leave
             const bool keep = live && !(a < p.prune);
-            const bool in_hbm = ia < ni_hbm;
-            const uint64_t kept_hbm = __ballot(keep && in_hbm);
-            const uint64_t kept_lds = __ballot(keep && !in_hbm);
-            uint32_t rank_h, count_h, rank_l, count_l;
-            group_rank<NG>(kept_hbm, lane, ga, rank_h, count_h);
-            group_rank<NG>(kept_lds, lane, ga, rank_l, count_l);
-            hbm_end = static_cast<int>(__builtin_amdgcn_readfirstlane(wave_max(count_h)));
-            lds_end = hbm_end + static_cast<int>(__builtin_amdgcn_readfirstlane(wave_max(count_l)));
-            slots[wave][lane] = dead_slot<NC>(ia < hbm_end ? kOutOfRange : 0u);
-            wave_lds_sync();
-            if (keep)
-                slots[wave][(in_hbm ? rank_h : hbm_end + rank_l) * NG + ga] = sl;
+            slots[wave][lane] = keep ? sl : dead_slot<NC>(ia < ni_hbm ? kOutOfRange : 0u);
         } else {
             slots[wave][lane] = sl;
         }
