@@ -12,6 +12,11 @@ pipeline (torch softmax + add, then msda_forward) is timed beside it; with
 ``--op forward_pruned`` one msda_forward_pruned call at ``--prune-threshold``
 (the fraction of samples it drops and the unpruned kernel's time on the same
 inputs are reported beside it).
+Queries are visited in a Z-order (Morton) order of the pixels when the
+workload's queries are the pyramid's pixel centres (``--query-order``; the
+order depends only on the level shapes, so it is built once, before the timed
+steps, like any per-shape plan); every output is the same as in the raw
+query order, which ``--query-order none`` times.
 Steps cycle over several distinct copies of the inputs whose total exceeds
 twice the 256 MB Infinity Cache, so each step reads its inputs from HBM
 rather than from a cache warmed by the previous step.
@@ -118,8 +123,9 @@ def backward_byte_counts(w):
     return U, G
 
 
-def counters_for(workload_name: str, op: str = "forward"):
-    """Per-launch HBM traffic from committed rocprofv3 counters, if current."""
+def counters_for(workload_name: str, op: str = "forward", query_order: str = "none"):
+    """Per-launch HBM traffic from committed rocprofv3 counters, if they were
+    taken from the current kernel sources with the same query order."""
     path = COUNTERS_FILES[op]
     if not os.path.exists(path):
         return None
@@ -128,7 +134,7 @@ def counters_for(workload_name: str, op: str = "forward"):
     if data.get("kernel_source_digest") != kernel_source_digest(op):
         return None
     entry = data.get("workloads", {}).get(workload_name)
-    if not entry:
+    if not entry or entry.get("query_order", "none") != query_order:
         return None
     return entry.get("traffic_bytes_per_launch")
 
@@ -329,6 +335,11 @@ def main(argv=None):
                     help="attention-weight threshold of --op forward_pruned "
                          "(default 0.8 / (L*P): about half the samples of softmaxed "
                          "N(0,1) logits)")
+    ap.add_argument("--query-order", choices=("auto", "none", "levels", "interleaved"),
+                    default="auto",
+                    help="visit order of the queries: a Z-order of the pixels with the "
+                         "levels interleaved or level by level, or none (the raw order); "
+                         "auto = interleaved for pixel-centre workloads, else none")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip timing the oracle (for profiler runs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -350,7 +361,8 @@ def main(argv=None):
     from scale_deformable_attention_02_amd import (msda3d_backward, msda3d_forward,
                                                    msda3d_forward_fused, msda3d_forward_pruned,
                                                    msda_backward, msda_forward,
-                                                   msda_forward_fused, msda_forward_pruned)
+                                                   msda_forward_fused, msda_forward_pruned,
+                                                   msda_query_order)
     from scale_deformable_attention_02_amd.workloads import (CONFIGS, make_fused_inputs,
                                                              make_grad_out, make_inputs)
 
@@ -372,6 +384,22 @@ def main(argv=None):
     if backward:
         base["grad_out"] = make_grad_out(w).to(dev)
     sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(copies - 1)]
+
+    order_kind = args.query_order
+    if order_kind == "auto":
+        order_kind = "interleaved" if w.queries == "pixel_centres" else "none"
+    if order_kind != "none" and w.queries != "pixel_centres":
+        print(f"bench.py: --query-order {order_kind} needs pixel-centre queries; "
+              f"{w.name} has {w.queries!r}", file=sys.stderr)
+        return 2
+    order, order_build_us = None, None
+    if order_kind != "none":
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        order = msda_query_order(w.shapes, order_kind == "levels", device=dev)
+        e1.record()
+        torch.cuda.synchronize()
+        order_build_us = e0.elapsed_time(e1) * 1e3
     if backward:
         outs = [(torch.empty_like(d["value"], dtype=torch.float32),
                  torch.empty_like(d["sampling_locations"]),
@@ -383,7 +411,8 @@ def main(argv=None):
             gv, gl, ga = outs[i % copies]
             bwd(d["value"], d["spatial_shapes"], d["level_start_index"],
                 d["sampling_locations"], d["attention_weights"], d["grad_out"],
-                grad_value=gv, grad_sampling_locations=gl, grad_attention_weights=ga)
+                grad_value=gv, grad_sampling_locations=gl, grad_attention_weights=ga,
+                query_order=order)
     elif fused:
         out_dt = torch.bfloat16 if w.out_dtype == "bf16" else torch.float32
         outs = [torch.empty((w.N, w.queries_per_image, w.M * w.D), dtype=out_dt, device=dev)
@@ -394,7 +423,8 @@ def main(argv=None):
         def step(i):
             d = sets[i % copies]
             ffn(d["value"], d["spatial_shapes"], d["level_start_index"], d["reference_points"],
-                d["sampling_offsets"], d["attention_logits"], out=outs[i % copies])
+                d["sampling_offsets"], d["attention_logits"], out=outs[i % copies],
+                query_order=order)
 
         def unfused_step(i):
             d = sets[i % copies]
@@ -402,7 +432,7 @@ def main(argv=None):
             loc = d["reference_points"].reshape(N, Lq, 1, 1, 1, dims) + d["sampling_offsets"]
             attw = torch.softmax(d["attention_logits"].reshape(N, Lq, M, L * P), dim=-1)
             fwd(d["value"], d["spatial_shapes"], d["level_start_index"], loc,
-                attw.reshape(N, Lq, M, L, P), out=outs[i % copies])
+                attw.reshape(N, Lq, M, L, P), out=outs[i % copies], query_order=order)
     elif pruned:
         out_dt = torch.bfloat16 if w.out_dtype == "bf16" else torch.float32
         outs = [torch.empty((w.N, w.queries_per_image, w.M * w.D), dtype=out_dt, device=dev)
@@ -414,12 +444,13 @@ def main(argv=None):
             d = sets[i % copies]
             pfn(d["value"], d["spatial_shapes"], d["level_start_index"],
                 d["sampling_locations"], d["attention_weights"], threshold,
-                out=outs[i % copies])
+                out=outs[i % copies], query_order=order)
 
         def unfused_step(i):  # the unpruned kernel on the same inputs
             d = sets[i % copies]
             fwd(d["value"], d["spatial_shapes"], d["level_start_index"],
-                d["sampling_locations"], d["attention_weights"], out=outs[i % copies])
+                d["sampling_locations"], d["attention_weights"], out=outs[i % copies],
+                query_order=order)
     else:
         out_dt = torch.bfloat16 if w.out_dtype == "bf16" else torch.float32
         outs = [torch.empty((w.N, w.queries_per_image, w.M * w.D), dtype=out_dt, device=dev)
@@ -429,7 +460,8 @@ def main(argv=None):
         def step(i):
             d = sets[i % copies]
             fwd(d["value"], d["spatial_shapes"], d["level_start_index"],
-                d["sampling_locations"], d["attention_weights"], out=outs[i % copies])
+                d["sampling_locations"], d["attention_weights"], out=outs[i % copies],
+                query_order=order)
 
     for i in range(args.warmup):
         step(i)
@@ -474,7 +506,10 @@ def main(argv=None):
     points = w.sampled_points
     ms_per_step = wall / args.steps * 1e3
     achieved = U / kernel_s / 1e9
-    traffic = counters_for(w.name, args.op)
+    order_label = ("none" if order is None else
+                   "z-order, levels interleaved" if order_kind == "interleaved"
+                   else "z-order, level by level")
+    traffic = counters_for(w.name, args.op, order_label)
     result = {
         "metric": (METRIC_BACKWARD if backward else METRIC_FUSED if fused
                    else METRIC_PRUNED if pruned else METRIC),
@@ -494,12 +529,14 @@ def main(argv=None):
             "Lq": w.queries_per_image, "M": w.M, "D": w.D, "L": w.L, "P": w.P,
             "value_dtype": w.value_dtype, "out_dtype": w.out_dtype,
             "op": args.op, "input_copies_cycled": copies,
+            "query_order": order_label,
             "parallelism": "single GPU",
         },
         "achieved_hbm_gbps": achieved,
         "gathered_gbps": G / kernel_s / 1e9,
         "kernel_us_mean": kernel_s * 1e6,
         "kernel_us_warm": warm_s * 1e6,
+        "query_order_build_us": order_build_us,
         "bytes_per_launch": {"compulsory": U, "gathered": G},
         "unfused_pipeline_us_per_step": unfused_us if fused else None,
         "unpruned_us_per_step": unfused_us if pruned else None,

@@ -75,7 +75,8 @@ typedef enum {
                                  weights not 4-byte aligned, shapes/starts
                                  not 8-byte aligned                        */
     MSDA_ERR_OVERFLOW = 6,    /* one image's value (S*M*D elements) is
-                                 2^31 bytes or more                        */
+                                 2^31 bytes or more (with a query order:
+                                 also its locations)                       */
     MSDA_ERR_LAUNCH = 7       /* the HIP launch failed                     */
 } msda_status;
 
@@ -89,9 +90,28 @@ typedef enum {
  *   attention_weights   float [N][Lq][M][L][P]
  *   out                 [N][Lq][M*D], out_dtype, fully overwritten
  *   out_dtype           MSDA_F32 (the fp32 accumulator) or MSDA_BF16
+ *   query_order         NULL, or int32 [Lq]: the order in which the queries
+ *                       are visited (see "Query order" below)
  *   stream              hipStream_t (void* so this header needs no HIP)
  *
  * N == 0 or Lq == 0 is a successful no-op (pointers may then be NULL).
+ *
+ * Query order (every forward and backward entry point).  With query_order
+ * NULL the kernels visit queries 0, 1, ..., Lq-1 of each (image, head) in
+ * turn.  Otherwise query_order is a device array of Lq int32, a permutation
+ * of 0..Lq-1 shared by all N images, and visit position r takes query
+ * query_order[r].  It changes the schedule only: every query still reads its
+ * own input rows and writes its own output rows, and the outputs equal those
+ * with NULL bit for bit (grad_value: up to the order of its atomic
+ * additions).  Queries whose samples fall on nearby pixels, visited
+ * together, share cached value rows, and in the backward merge their
+ * grad_value additions: msda_query_order below builds such an order for
+ * queries that are the pyramid's pixel centres.  An entry >= Lq (or
+ * negative) is read as Lq-1, so an array that is not a permutation gives
+ * wrong outputs but no access outside the tensors.  Extra limits with an
+ * order: it is 4-byte aligned (MSDA_ERR_ALIGN), and one image's locations
+ * (backward: also its output gradient) are below 2^31 bytes, so that a launch
+ * covers whole images (MSDA_ERR_OVERFLOW).
  */
 int msda_forward(const void* value, int value_dtype,
                  const int64_t* spatial_shapes,
@@ -99,7 +119,8 @@ int msda_forward(const void* value, int value_dtype,
                  const float* sampling_locations,
                  const float* attention_weights, void* out, int out_dtype,
                  int64_t N, int64_t S, int64_t M, int64_t D,
-                 int64_t Lq, int64_t L, int64_t P, void* stream);
+                 int64_t Lq, int64_t L, int64_t P,
+                 const int32_t* query_order, void* stream);
 
 /*
  * 3D multi-scale deformable attention forward (trilinear over 8 corners).
@@ -114,7 +135,8 @@ int msda3d_forward(const void* value, int value_dtype,
                    const float* sampling_locations,
                    const float* attention_weights, void* out, int out_dtype,
                    int64_t N, int64_t S, int64_t M, int64_t D,
-                   int64_t Lq, int64_t L, int64_t P, void* stream);
+                   int64_t Lq, int64_t L, int64_t P,
+                   const int32_t* query_order, void* stream);
 
 /*
  * 2D forward with probability-aware point pruning (DEFA, abstract: sampling
@@ -135,7 +157,8 @@ int msda_forward_pruned(const void* value, int value_dtype,
                         float threshold,
                         void* out, int out_dtype,
                         int64_t N, int64_t S, int64_t M, int64_t D,
-                        int64_t Lq, int64_t L, int64_t P, void* stream);
+                        int64_t Lq, int64_t L, int64_t P,
+                        const int32_t* query_order, void* stream);
 
 /* 3D counterpart of msda_forward_pruned. */
 int msda3d_forward_pruned(const void* value, int value_dtype,
@@ -146,7 +169,8 @@ int msda3d_forward_pruned(const void* value, int value_dtype,
                           float threshold,
                           void* out, int out_dtype,
                           int64_t N, int64_t S, int64_t M, int64_t D,
-                          int64_t Lq, int64_t L, int64_t P, void* stream);
+                          int64_t Lq, int64_t L, int64_t P,
+                          const int32_t* query_order, void* stream);
 
 /*
  * 2D forward with the module's front end fused into the kernel.  Instead of
@@ -171,7 +195,8 @@ int msda_forward_fused(const void* value, int value_dtype,
                        const float* attention_logits,
                        void* out, int out_dtype,
                        int64_t N, int64_t S, int64_t M, int64_t D,
-                       int64_t Lq, int64_t L, int64_t P, void* stream);
+                       int64_t Lq, int64_t L, int64_t P,
+                       const int32_t* query_order, void* stream);
 
 /* 3D counterpart: reference_points [N][Lq][3], offsets [...][3]. */
 int msda3d_forward_fused(const void* value, int value_dtype,
@@ -182,7 +207,8 @@ int msda3d_forward_fused(const void* value, int value_dtype,
                          const float* attention_logits,
                          void* out, int out_dtype,
                          int64_t N, int64_t S, int64_t M, int64_t D,
-                         int64_t Lq, int64_t L, int64_t P, void* stream);
+                         int64_t Lq, int64_t L, int64_t P,
+                         const int32_t* query_order, void* stream);
 
 /*
  * 2D backward: gradients of a loss with respect to value, sampling_locations
@@ -216,7 +242,8 @@ int msda_backward(const void* value, int value_dtype,
                   float* grad_value, float* grad_sampling_locations,
                   float* grad_attention_weights,
                   int64_t N, int64_t S, int64_t M, int64_t D,
-                  int64_t Lq, int64_t L, int64_t P, void* stream);
+                  int64_t Lq, int64_t L, int64_t P,
+                  const int32_t* query_order, void* stream);
 
 /* 3D backward (trilinear); shapes [L][3], locations and their gradient
  * [N][Lq][M][L][P][3]; otherwise as msda_backward. */
@@ -229,7 +256,39 @@ int msda3d_backward(const void* value, int value_dtype,
                     float* grad_value, float* grad_sampling_locations,
                     float* grad_attention_weights,
                     int64_t N, int64_t S, int64_t M, int64_t D,
-                    int64_t Lq, int64_t L, int64_t P, void* stream);
+                    int64_t Lq, int64_t L, int64_t P,
+                    const int32_t* query_order, void* stream);
+
+/*
+ * Query order for pixel-centre queries: the queries are the centres of the
+ * pyramid's pixels in the flattened order of `value` (query s is pixel s, so
+ * Lq = S), as in an encoder whose queries are the feature pixels and whose
+ * reference point is the query's own position on the map ("What is
+ * Deformable Attention", reference position; "3D Attention That Knows Where
+ * to Look", recipe step 1).  Fills query_order with a permutation of 0..S-1
+ * for the query_order argument above.
+ *   spatial_shapes  HOST int64 [L][dims]: (H_l, W_l), or (Z_l, H_l, W_l)
+ *   dims            2 or 3
+ *   level_major     0: levels interleaved; nonzero: one level after another
+ *   query_order     device int32 [S], overwritten
+ * Each pixel is given the cell of a grid of 2^10 cells per axis over the unit
+ * square (cube) that holds its normalized centre: along an axis of extent E,
+ * pixel j has cell floor((2j+1) * 2^10 / (2E)).  Its key is the Z-order
+ * (Morton) code of the cell: bit b of the x cell at key bit dims*b, of y at
+ * dims*b+1, of z at dims*b+2.  The pixels are sorted by (key, level, index
+ * in the level) when level_major is 0, and by (level, key, index) otherwise;
+ * query_order[r] is the pixel of rank r.  The kernel counts each pixel's rank
+ * in closed form (boxes of the grid, one per key bit), so nothing is sorted
+ * and nothing is allocated.  Asynchronous on `stream`; the order depends on
+ * the shapes only and can be built once and reused.
+ * Errors: MSDA_ERR_NULL; MSDA_ERR_DIM (dims not 2 or 3, L < 1, an extent
+ * < 1, S not the pixel total); MSDA_ERR_UNSUPPORTED (L > 16, an extent
+ * >= 2^20); MSDA_ERR_OVERFLOW (S >= 2^31); MSDA_ERR_ALIGN (query_order not
+ * 4-byte aligned).
+ */
+int msda_query_order(const int64_t* spatial_shapes, int64_t L, int64_t dims,
+                     int level_major, int32_t* query_order, int64_t S,
+                     void* stream);
 
 /*
  * Dense projection on the matrix cores: y = x * weight^T + bias.

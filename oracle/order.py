@@ -1,0 +1,70 @@
+"""Oracle of the visit order for pixel-centre queries (test infrastructure only).
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+import this module; the HIP library never calls it and the two share no code.
+
+The queries are the centres of the pyramid's pixels in flattened order (query
+s is pixel s), the encoder case where each query's reference point is its own
+position on the feature map ("What is Deformable Attention", reference
+position; "3D Attention That Knows Where to Look", recipe step 1).  The order
+the library builds is defined as a sort: every pixel gets the cell of a grid
+of 2^10 cells per axis over the unit square (cube) that holds its normalized
+centre, floor((2j+1) * 2^10 / (2E)) along an axis of extent E; the cell's
+Z-order (Morton) key interleaves the cell coordinates bit by bit, x lowest;
+and the pixels are sorted by (key, level, index in the level), or by (level,
+key, index) for the level-major order.  This module computes exactly that
+with integer arithmetic and one stable sort (the library instead counts each
+pixel's rank in closed form, without sorting).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+CELL_BITS = 10
+
+
+def pixel_cells(shapes, dims: int):
+    """Per pixel of the flattened pyramid: (level, index in level, cell
+    coordinates [S, dims] with column 0 = x)."""
+    levels, index, cells = [], [], []
+    for l, shp in enumerate(shapes):
+        ext = [int(e) for e in shp]            # (H, W) or (Z, H, W)
+        n = int(np.prod(ext))
+        r = np.arange(n, dtype=np.int64)
+        # raster index -> coordinates, x (along W) fastest
+        coords = []
+        rest = r
+        for e in reversed(ext):                # W, then H, then Z
+            coords.append(rest % e)
+            rest = rest // e
+        c = np.stack([((2 * j + 1) << CELL_BITS) // (2 * e)
+                      for j, e in zip(coords, reversed(ext))], axis=1)
+        levels.append(np.full(n, l, dtype=np.int64))
+        index.append(r)
+        cells.append(c)
+    return np.concatenate(levels), np.concatenate(index), np.concatenate(cells)
+
+
+def morton_key(cells: np.ndarray) -> np.ndarray:
+    """Z-order key of cell coordinates [S, dims]: bit b of axis d goes to key
+    bit dims*b + d."""
+    dims = cells.shape[1]
+    key = np.zeros(cells.shape[0], dtype=np.int64)
+    for b in range(CELL_BITS):
+        for d in range(dims):
+            key |= ((cells[:, d] >> b) & 1) << (dims * b + d)
+    return key
+
+
+def query_order_oracle(shapes, level_major: bool) -> np.ndarray:
+    """The visit order (int64 [S]): entry r is the pixel of rank r."""
+    shapes = [tuple(int(e) for e in s) for s in shapes]
+    dims = len(shapes[0])
+    level, index, cells = pixel_cells(shapes, dims)
+    key = morton_key(cells)
+    # np.lexsort sorts by the last key first
+    if level_major:
+        order = np.lexsort((index, key, level))
+    else:
+        order = np.lexsort((index, level, key))
+    return order.astype(np.int64)

@@ -2,7 +2,8 @@
 
 ``msda_forward`` / ``msda3d_forward``, ``msda_forward_pruned`` /
 ``msda3d_forward_pruned``, ``msda_forward_fused`` / ``msda3d_forward_fused``
-and ``msda_backward`` / ``msda3d_backward``, and the projection ``msda_linear``
+and ``msda_backward`` / ``msda3d_backward``, the projection ``msda_linear`` and
+the visit-order builder ``msda_query_order``
 take torch tensors that already live on the GPU, check
 dtypes/shapes/contiguity, allocate outputs with torch when the caller passes
 none, and call the same-named C entry point of ``libmsda.so`` on torch's
@@ -37,7 +38,7 @@ STATUS = {
 # Every symbol include/msda.h declares.
 EXPORTED = ("msda_forward", "msda3d_forward", "msda_forward_pruned", "msda3d_forward_pruned",
             "msda_forward_fused", "msda3d_forward_fused", "msda_backward", "msda3d_backward",
-            "msda_linear", "msda_status_string")
+            "msda_linear", "msda_query_order", "msda_status_string")
 
 _lib = None
 
@@ -70,24 +71,26 @@ def load_library() -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [vp, ctypes.c_int, vp, vp, vp, vp, vp, ctypes.c_int,
-                       i64, i64, i64, i64, i64, i64, i64, vp]
+                       i64, i64, i64, i64, i64, i64, i64, vp, vp]
     for name in ("msda_forward_pruned", "msda3d_forward_pruned"):
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [vp, ctypes.c_int, vp, vp, vp, vp, ctypes.c_float, vp, ctypes.c_int,
-                       i64, i64, i64, i64, i64, i64, i64, vp]
+                       i64, i64, i64, i64, i64, i64, i64, vp, vp]
     for name in ("msda_forward_fused", "msda3d_forward_fused"):
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [vp, ctypes.c_int, vp, vp, vp, vp, vp, vp, ctypes.c_int,
-                       i64, i64, i64, i64, i64, i64, i64, vp]
+                       i64, i64, i64, i64, i64, i64, i64, vp, vp]
     for name in ("msda_backward", "msda3d_backward"):
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [vp, ctypes.c_int, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp,
-                       i64, i64, i64, i64, i64, i64, i64, vp]
+                       i64, i64, i64, i64, i64, i64, i64, vp, vp]
     lib.msda_linear.restype = ctypes.c_int
     lib.msda_linear.argtypes = [vp, ctypes.c_int, vp, vp, vp, ctypes.c_int, i64, i64, i64, vp]
+    lib.msda_query_order.restype = ctypes.c_int
+    lib.msda_query_order.argtypes = [vp, i64, i64, ctypes.c_int, vp, i64, vp]
     lib.msda_status_string.restype = ctypes.c_char_p
     lib.msda_status_string.argtypes = [ctypes.c_int]
     _lib = lib
@@ -101,47 +104,48 @@ def status_string(status: int) -> str:
 def raw_call(dims: int, value_ptr: int, value_dtype: int, shapes_ptr: int,
              starts_ptr: int, loc_ptr: int, attw_ptr: int, out_ptr: int,
              out_dtype: int, N: int, S: int, M: int, D: int, Lq: int, L: int, P: int,
-             stream: int = 0) -> int:
-    """Call the C entry point with raw pointers; returns the msda_status."""
+             stream: int = 0, order_ptr: int = 0) -> int:
+    """Call the C entry point with raw pointers (``order_ptr``: the query
+    order, 0 for none); returns the msda_status."""
     lib = load_library()
     fn = lib.msda_forward if dims == 2 else lib.msda3d_forward
     return fn(value_ptr, value_dtype, shapes_ptr, starts_ptr, loc_ptr, attw_ptr,
-              out_ptr, out_dtype, N, S, M, D, Lq, L, P, stream)
+              out_ptr, out_dtype, N, S, M, D, Lq, L, P, order_ptr, stream)
 
 
 def raw_pruned_call(dims: int, value_ptr: int, value_dtype: int, shapes_ptr: int,
                     starts_ptr: int, loc_ptr: int, attw_ptr: int, threshold: float, out_ptr: int,
                     out_dtype: int, N: int, S: int, M: int, D: int, Lq: int, L: int, P: int,
-                    stream: int = 0) -> int:
+                    stream: int = 0, order_ptr: int = 0) -> int:
     """Call the pruned forward with raw pointers; returns the msda_status."""
     lib = load_library()
     fn = lib.msda_forward_pruned if dims == 2 else lib.msda3d_forward_pruned
     return fn(value_ptr, value_dtype, shapes_ptr, starts_ptr, loc_ptr, attw_ptr, threshold,
-              out_ptr, out_dtype, N, S, M, D, Lq, L, P, stream)
+              out_ptr, out_dtype, N, S, M, D, Lq, L, P, order_ptr, stream)
 
 
 def raw_fused_call(dims: int, value_ptr: int, value_dtype: int, shapes_ptr: int,
                    starts_ptr: int, ref_ptr: int, off_ptr: int, logits_ptr: int, out_ptr: int,
                    out_dtype: int, N: int, S: int, M: int, D: int, Lq: int, L: int, P: int,
-                   stream: int = 0) -> int:
+                   stream: int = 0, order_ptr: int = 0) -> int:
     """Call the fused-front-end forward with raw pointers; returns the msda_status."""
     lib = load_library()
     fn = lib.msda_forward_fused if dims == 2 else lib.msda3d_forward_fused
     return fn(value_ptr, value_dtype, shapes_ptr, starts_ptr, ref_ptr, off_ptr, logits_ptr,
-              out_ptr, out_dtype, N, S, M, D, Lq, L, P, stream)
+              out_ptr, out_dtype, N, S, M, D, Lq, L, P, order_ptr, stream)
 
 
 def raw_backward_call(dims: int, value_ptr: int, value_dtype: int, shapes_ptr: int,
                       starts_ptr: int, loc_ptr: int, attw_ptr: int, grad_out_ptr: int,
                       grad_out_dtype: int, grad_value_ptr: int, grad_loc_ptr: int,
                       grad_attw_ptr: int, N: int, S: int, M: int, D: int, Lq: int, L: int,
-                      P: int, stream: int = 0) -> int:
+                      P: int, stream: int = 0, order_ptr: int = 0) -> int:
     """Call the backward C entry point with raw pointers; returns the msda_status."""
     lib = load_library()
     fn = lib.msda_backward if dims == 2 else lib.msda3d_backward
     return fn(value_ptr, value_dtype, shapes_ptr, starts_ptr, loc_ptr, attw_ptr,
               grad_out_ptr, grad_out_dtype, grad_value_ptr, grad_loc_ptr, grad_attw_ptr,
-              N, S, M, D, Lq, L, P, stream)
+              N, S, M, D, Lq, L, P, order_ptr, stream)
 
 
 def _dtype_code(dtype: torch.dtype, what: str) -> int:
@@ -182,12 +186,25 @@ def _check_inputs(dims, value, spatial_shapes, level_start_index, sampling_locat
     return code, N, S, M, D, Lq, L, P
 
 
+def _order_ptr(query_order: Optional[torch.Tensor], Lq: int, device) -> int:
+    """Pointer of a validated query order (int32 [Lq] on ``device``), or 0."""
+    if query_order is None:
+        return 0
+    if (not query_order.is_cuda or query_order.device != device
+            or query_order.dtype != torch.int32 or tuple(query_order.shape) != (Lq,)
+            or not query_order.is_contiguous()):
+        raise ValueError(f"query_order must be a contiguous int32 [{Lq}] tensor on value's "
+                         "device")
+    return query_order.data_ptr()
+
+
 def _forward(dims: int, value: torch.Tensor, spatial_shapes: torch.Tensor,
              level_start_index: torch.Tensor, sampling_locations: torch.Tensor,
              attention_weights: torch.Tensor, out: Optional[torch.Tensor],
              out_dtype: Optional[torch.dtype],
              stream: Optional[torch.cuda.Stream],
-             threshold: Optional[float] = None) -> torch.Tensor:
+             threshold: Optional[float] = None,
+             query_order: Optional[torch.Tensor] = None) -> torch.Tensor:
     code, N, S, M, D, Lq, L, P = _check_inputs(dims, value, spatial_shapes, level_start_index,
                                                sampling_locations, attention_weights)
     if out is None:
@@ -197,45 +214,50 @@ def _forward(dims: int, value: torch.Tensor, spatial_shapes: torch.Tensor,
           or out.device != value.device or (out_dtype is not None and out.dtype != out_dtype)):
         raise ValueError("out must be a contiguous [N, Lq, M*D] tensor on value's device")
     out_code = _dtype_code(out.dtype, "out")
+    order = _order_ptr(query_order, Lq, value.device)
     s = stream if stream is not None else torch.cuda.current_stream(value.device)
     if threshold is None:
         status = raw_call(dims, value.data_ptr(), code, spatial_shapes.data_ptr(),
                           level_start_index.data_ptr(), sampling_locations.data_ptr(),
                           attention_weights.data_ptr(), out.data_ptr(), out_code,
-                          N, S, M, D, Lq, L, P, s.cuda_stream)
+                          N, S, M, D, Lq, L, P, s.cuda_stream, order)
     else:
         status = raw_pruned_call(dims, value.data_ptr(), code, spatial_shapes.data_ptr(),
                                  level_start_index.data_ptr(), sampling_locations.data_ptr(),
                                  attention_weights.data_ptr(), float(threshold), out.data_ptr(),
-                                 out_code, N, S, M, D, Lq, L, P, s.cuda_stream)
+                                 out_code, N, S, M, D, Lq, L, P, s.cuda_stream, order)
     if status != 0:
         raise MsdaError(status, status_string(status))
     return out
 
 
 def msda_forward(value, spatial_shapes, level_start_index, sampling_locations,
-                 attention_weights, out=None, out_dtype=None, stream=None) -> torch.Tensor:
+                 attention_weights, out=None, out_dtype=None, stream=None,
+                 query_order=None) -> torch.Tensor:
     """2D MSDA forward: value [N,S,M,D] (fp32/bf16), spatial_shapes [L,2]=(H,W),
     level_start_index [L], sampling_locations [N,Lq,M,L,P,2], attention_weights
     [N,Lq,M,L,P]; returns [N, Lq, M*D].  The output dtype is ``out``'s, else
     ``out_dtype``, else value's (fp32 accumulation either way; bf16 output is
-    rounded to nearest-even).  Asynchronous on ``stream`` (default: torch's
-    current stream)."""
+    rounded to nearest-even).  ``query_order`` (int32 [Lq] on the GPU, a
+    permutation, e.g. from ``msda_query_order``) sets the order in which the
+    queries are visited; the result is the same.  Asynchronous on ``stream``
+    (default: torch's current stream)."""
     return _forward(2, value, spatial_shapes, level_start_index, sampling_locations,
-                    attention_weights, out, out_dtype, stream)
+                    attention_weights, out, out_dtype, stream, query_order=query_order)
 
 
 def msda3d_forward(value, spatial_shapes, level_start_index, sampling_locations,
-                   attention_weights, out=None, out_dtype=None, stream=None) -> torch.Tensor:
+                   attention_weights, out=None, out_dtype=None, stream=None,
+                   query_order=None) -> torch.Tensor:
     """3D MSDA forward (trilinear): spatial_shapes [L,3]=(Z,H,W), locations
     [N,Lq,M,L,P,3] = (x, y, z); otherwise as ``msda_forward``."""
     return _forward(3, value, spatial_shapes, level_start_index, sampling_locations,
-                    attention_weights, out, out_dtype, stream)
+                    attention_weights, out, out_dtype, stream, query_order=query_order)
 
 
 def _backward(dims, value, spatial_shapes, level_start_index, sampling_locations,
               attention_weights, grad_out, grad_value, grad_sampling_locations,
-              grad_attention_weights, stream):
+              grad_attention_weights, stream, query_order=None):
     code, N, S, M, D, Lq, L, P = _check_inputs(dims, value, spatial_shapes, level_start_index,
                                                sampling_locations, attention_weights)
     if not grad_out.is_cuda or not grad_out.is_contiguous() or grad_out.shape != (N, Lq, M * D):
@@ -255,12 +277,13 @@ def _backward(dims, value, spatial_shapes, level_start_index, sampling_locations
     gl = _out(grad_sampling_locations, tuple(sampling_locations.shape),
               "grad_sampling_locations")
     ga = _out(grad_attention_weights, tuple(attention_weights.shape), "grad_attention_weights")
+    order = _order_ptr(query_order, Lq, dev)
     s = stream if stream is not None else torch.cuda.current_stream(dev)
     status = raw_backward_call(dims, value.data_ptr(), code, spatial_shapes.data_ptr(),
                                level_start_index.data_ptr(), sampling_locations.data_ptr(),
                                attention_weights.data_ptr(), grad_out.data_ptr(), gcode,
                                gv.data_ptr(), gl.data_ptr(), ga.data_ptr(),
-                               N, S, M, D, Lq, L, P, s.cuda_stream)
+                               N, S, M, D, Lq, L, P, s.cuda_stream, order)
     if status != 0:
         raise MsdaError(status, status_string(status))
     return gv, gl, ga
@@ -269,48 +292,50 @@ def _backward(dims, value, spatial_shapes, level_start_index, sampling_locations
 def msda_backward(value, spatial_shapes, level_start_index, sampling_locations,
                   attention_weights, grad_out, grad_value=None,
                   grad_sampling_locations=None, grad_attention_weights=None,
-                  stream=None):
+                  stream=None, query_order=None):
     """2D MSDA backward: given ``grad_out`` [N, Lq, M*D] (fp32 or bf16) returns
     float32 ``(grad_value [N,S,M,D], grad_sampling_locations [N,Lq,M,L,P,2],
     grad_attention_weights [N,Lq,M,L,P])``; all three are overwritten (passed
     tensors are reused).  grad_value is accumulated with fp32 atomics, so its
-    last bits may differ between runs.  Asynchronous on ``stream``."""
+    last bits may differ between runs.  ``query_order`` as in
+    ``msda_forward``.  Asynchronous on ``stream``."""
     return _backward(2, value, spatial_shapes, level_start_index, sampling_locations,
                      attention_weights, grad_out, grad_value, grad_sampling_locations,
-                     grad_attention_weights, stream)
+                     grad_attention_weights, stream, query_order)
 
 
 def msda3d_backward(value, spatial_shapes, level_start_index, sampling_locations,
                     attention_weights, grad_out, grad_value=None,
                     grad_sampling_locations=None, grad_attention_weights=None,
-                    stream=None):
+                    stream=None, query_order=None):
     """3D MSDA backward (trilinear); see ``msda_backward``."""
     return _backward(3, value, spatial_shapes, level_start_index, sampling_locations,
                      attention_weights, grad_out, grad_value, grad_sampling_locations,
-                     grad_attention_weights, stream)
+                     grad_attention_weights, stream, query_order)
 
 
 def msda_forward_pruned(value, spatial_shapes, level_start_index, sampling_locations,
                         attention_weights, threshold, out=None, out_dtype=None,
-                        stream=None) -> torch.Tensor:
+                        stream=None, query_order=None) -> torch.Tensor:
     """2D MSDA forward with probability-aware point pruning: samples whose
     attention weight is below ``threshold`` (an fp32 value) are skipped, the
     others keep their weights (no renormalisation); otherwise as
     ``msda_forward``."""
     return _forward(2, value, spatial_shapes, level_start_index, sampling_locations,
-                    attention_weights, out, out_dtype, stream, threshold)
+                    attention_weights, out, out_dtype, stream, threshold, query_order)
 
 
 def msda3d_forward_pruned(value, spatial_shapes, level_start_index, sampling_locations,
                           attention_weights, threshold, out=None, out_dtype=None,
-                          stream=None) -> torch.Tensor:
+                          stream=None, query_order=None) -> torch.Tensor:
     """3D counterpart of ``msda_forward_pruned``."""
     return _forward(3, value, spatial_shapes, level_start_index, sampling_locations,
-                    attention_weights, out, out_dtype, stream, threshold)
+                    attention_weights, out, out_dtype, stream, threshold, query_order)
 
 
 def _forward_fused(dims, value, spatial_shapes, level_start_index, reference_points,
-                   sampling_offsets, attention_logits, out, out_dtype, stream):
+                   sampling_offsets, attention_logits, out, out_dtype, stream,
+                   query_order=None):
     code, N, S, M, D, Lq, L, P = _check_inputs(dims, value, spatial_shapes, level_start_index,
                                                sampling_offsets, attention_logits)
     if (not reference_points.is_cuda or not reference_points.is_contiguous()
@@ -325,11 +350,13 @@ def _forward_fused(dims, value, spatial_shapes, level_start_index, reference_poi
           or out.device != value.device or (out_dtype is not None and out.dtype != out_dtype)):
         raise ValueError("out must be a contiguous [N, Lq, M*D] tensor on value's device")
     out_code = _dtype_code(out.dtype, "out")
+    order = _order_ptr(query_order, Lq, value.device)
     s = stream if stream is not None else torch.cuda.current_stream(value.device)
     status = raw_fused_call(dims, value.data_ptr(), code, spatial_shapes.data_ptr(),
                             level_start_index.data_ptr(), reference_points.data_ptr(),
                             sampling_offsets.data_ptr(), attention_logits.data_ptr(),
-                            out.data_ptr(), out_code, N, S, M, D, Lq, L, P, s.cuda_stream)
+                            out.data_ptr(), out_code, N, S, M, D, Lq, L, P, s.cuda_stream,
+                            order)
     if status != 0:
         raise MsdaError(status, status_string(status))
     return out
@@ -337,21 +364,23 @@ def _forward_fused(dims, value, spatial_shapes, level_start_index, reference_poi
 
 def msda_forward_fused(value, spatial_shapes, level_start_index, reference_points,
                        sampling_offsets, attention_logits, out=None, out_dtype=None,
-                       stream=None) -> torch.Tensor:
+                       stream=None, query_order=None) -> torch.Tensor:
     """2D MSDA forward with the front end fused: attention weights = softmax of
     ``attention_logits`` [N,Lq,M,L,P] over the L*P samples of each (n, q, m),
     locations = ``reference_points`` [N,Lq,2] + ``sampling_offsets``
     [N,Lq,M,L,P,2] (fp32); otherwise as ``msda_forward``."""
     return _forward_fused(2, value, spatial_shapes, level_start_index, reference_points,
-                          sampling_offsets, attention_logits, out, out_dtype, stream)
+                          sampling_offsets, attention_logits, out, out_dtype, stream,
+                          query_order)
 
 
 def msda3d_forward_fused(value, spatial_shapes, level_start_index, reference_points,
                          sampling_offsets, attention_logits, out=None, out_dtype=None,
-                         stream=None) -> torch.Tensor:
+                         stream=None, query_order=None) -> torch.Tensor:
     """3D counterpart of ``msda_forward_fused`` (3-component points)."""
     return _forward_fused(3, value, spatial_shapes, level_start_index, reference_points,
-                          sampling_offsets, attention_logits, out, out_dtype, stream)
+                          sampling_offsets, attention_logits, out, out_dtype, stream,
+                          query_order)
 
 
 def raw_linear_call(x_ptr: int, x_dtype: int, w_ptr: int, bias_ptr: int, y_ptr: int,
@@ -389,6 +418,41 @@ def msda_linear(x, weight, bias=None, out=None, out_dtype=None, stream=None) -> 
     status = raw_linear_call(x.data_ptr(), code, weight.data_ptr(),
                              0 if bias is None else bias.data_ptr(), out.data_ptr(), ycode,
                              R, K, N, s.cuda_stream)
+    if status != 0:
+        raise MsdaError(status, status_string(status))
+    return out
+
+
+def raw_query_order_call(shapes_ptr: int, L: int, dims: int, level_major: int, order_ptr: int,
+                         S: int, stream: int = 0) -> int:
+    """Call msda_query_order with raw pointers (shapes on the host); returns
+    the msda_status."""
+    return load_library().msda_query_order(shapes_ptr, L, dims, level_major, order_ptr, S,
+                                           stream)
+
+
+def msda_query_order(spatial_shapes, level_major: bool = True, device=None, out=None,
+                     stream=None) -> torch.Tensor:
+    """Visit order for queries that are the pyramid's pixel centres (query s is
+    pixel s): int32 [S] on ``device`` (default: the current GPU), the pixels
+    ranked by the Z-order key of their normalized centre on a 2^10 grid per
+    axis, level by level (``level_major``) or with the levels interleaved.
+    ``spatial_shapes`` is [L, 2] = (H, W) or [L, 3] = (Z, H, W) (a tensor on
+    any device, or nested sequences); it is read on the host."""
+    shapes = torch.as_tensor(spatial_shapes, dtype=torch.int64).cpu().contiguous()
+    if shapes.dim() != 2 or shapes.shape[1] not in (2, 3):
+        raise ValueError("spatial_shapes must be [L, 2] or [L, 3]")
+    L, dims = shapes.shape
+    S = int(torch.prod(shapes, dim=1).sum())
+    if out is None:
+        dev = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+        out = torch.empty((S,), dtype=torch.int32, device=dev)
+    elif (not out.is_cuda or out.dtype != torch.int32 or tuple(out.shape) != (S,)
+          or not out.is_contiguous()):
+        raise ValueError(f"out must be a contiguous int32 [{S}] GPU tensor")
+    s = stream if stream is not None else torch.cuda.current_stream(out.device)
+    status = raw_query_order_call(shapes.data_ptr(), L, dims, 1 if level_major else 0,
+                                  out.data_ptr(), S, s.cuda_stream)
     if status != 0:
         raise MsdaError(status, status_string(status))
     return out

@@ -111,8 +111,8 @@ int forward(const void* value, int value_dtype, const int64_t* spatial_shapes,
             const int64_t* level_start_index, const float* sampling_locations,
             const float* attention_weights, void* out, int out_dtype, int64_t N,
             int64_t S, int64_t M, int64_t D, int64_t Lq, int64_t L, int64_t P,
-            void* stream, const float* reference_points = nullptr,
-            float prune_threshold = 0.0f) {
+            const int32_t* query_order, void* stream,
+            const float* reference_points = nullptr, float prune_threshold = 0.0f) {
     if (N < 0 || Lq < 0 || S < 1 || M < 1 || D < 1 || L < 1 || P < 1)
         return MSDA_ERR_DIM;
     if (!known_dtype(value_dtype) || !known_dtype(out_dtype)) return MSDA_ERR_DTYPE;
@@ -130,7 +130,8 @@ int forward(const void* value, int value_dtype, const int64_t* spatial_shapes,
 
     if (!aligned(value, 16) || !aligned(out, 16) || !aligned(sampling_locations, 4) ||
         !aligned(attention_weights, 4) || !aligned(spatial_shapes, 8) ||
-        !aligned(level_start_index, 8) || (FUSED && !aligned(reference_points, 4)))
+        !aligned(level_start_index, 8) || (FUSED && !aligned(reference_points, 4)) ||
+        !aligned(query_order, 4))
         return MSDA_ERR_ALIGN;
 
     // One image's value must be addressable with 32-bit byte offsets.
@@ -151,12 +152,15 @@ int forward(const void* value, int value_dtype, const int64_t* spatial_shapes,
 
     // Work per launch: whole images while the value slice, the locations and
     // the tile count stay below 2^31 bytes / 2^30 tiles (32-bit buffer
-    // offsets); otherwise one image at a time, split into query ranges.
+    // offsets); otherwise one image at a time, split into query ranges (not
+    // with a visit order, whose positions address any query of the image).
     const int64_t loc_per_query = M * LP * DIM * 4;
     const int64_t attw_per_query = M * LP * 4;
     const int64_t kTileLimit = int64_t{1} << 30;
+    const bool whole_images = Lq * loc_per_query < kLimit && Lq * M < kTileLimit;
+    if (query_order && !whole_images) return MSDA_ERR_OVERFLOW;
     int64_t nb = 0, nq = Lq;
-    if (Lq * loc_per_query < kLimit && Lq * M < kTileLimit) {
+    if (whole_images) {
         nb = (kLimit - 1) / image_bytes;
         const int64_t by_loc = (kLimit - 1) / (Lq * loc_per_query);
         const int64_t by_tiles = (kTileLimit - 1) / (Lq * M);
@@ -221,6 +225,7 @@ int forward(const void* value, int value_dtype, const int64_t* spatial_shapes,
                 p.ref_bytes = static_cast<uint32_t>(nbatch * nquery * DIM * 4);
             }
             p.prune = prune_threshold;
+            p.order = query_order;   // whole images: q0 == 0 and nquery == Lq
 
             // Staged kernel: large 2D launches whose phase-B iterations are
             // level-pure (G divides P), with MSDA_STAGED_WGS_PER_SLICE
@@ -264,60 +269,62 @@ int msda_forward(const void* value, int value_dtype, const int64_t* spatial_shap
                  const int64_t* level_start_index, const float* sampling_locations,
                  const float* attention_weights, void* out, int out_dtype, int64_t N,
                  int64_t S, int64_t M, int64_t D, int64_t Lq, int64_t L, int64_t P,
-                 void* stream) {
+                 const int32_t* query_order, void* stream) {
     return forward<2, false>(value, value_dtype, spatial_shapes, level_start_index,
                              sampling_locations, attention_weights, out, out_dtype, N, S, M, D,
-                             Lq, L, P, stream);
+                             Lq, L, P, query_order, stream);
 }
 
 int msda3d_forward(const void* value, int value_dtype, const int64_t* spatial_shapes,
                    const int64_t* level_start_index, const float* sampling_locations,
                    const float* attention_weights, void* out, int out_dtype, int64_t N,
                    int64_t S, int64_t M, int64_t D, int64_t Lq, int64_t L, int64_t P,
-                   void* stream) {
+                   const int32_t* query_order, void* stream) {
     return forward<3, false>(value, value_dtype, spatial_shapes, level_start_index,
                              sampling_locations, attention_weights, out, out_dtype, N, S, M, D,
-                             Lq, L, P, stream);
+                             Lq, L, P, query_order, stream);
 }
 
 int msda_forward_pruned(const void* value, int value_dtype, const int64_t* spatial_shapes,
                         const int64_t* level_start_index, const float* sampling_locations,
                         const float* attention_weights, float threshold, void* out,
                         int out_dtype, int64_t N, int64_t S, int64_t M, int64_t D, int64_t Lq,
-                        int64_t L, int64_t P, void* stream) {
+                        int64_t L, int64_t P, const int32_t* query_order, void* stream) {
     return forward<2, false, true>(value, value_dtype, spatial_shapes, level_start_index,
                                    sampling_locations, attention_weights, out, out_dtype, N, S,
-                                   M, D, Lq, L, P, stream, nullptr, threshold);
+                                   M, D, Lq, L, P, query_order, stream, nullptr, threshold);
 }
 
 int msda3d_forward_pruned(const void* value, int value_dtype, const int64_t* spatial_shapes,
                           const int64_t* level_start_index, const float* sampling_locations,
                           const float* attention_weights, float threshold, void* out,
                           int out_dtype, int64_t N, int64_t S, int64_t M, int64_t D,
-                          int64_t Lq, int64_t L, int64_t P, void* stream) {
+                          int64_t Lq, int64_t L, int64_t P, const int32_t* query_order,
+                          void* stream) {
     return forward<3, false, true>(value, value_dtype, spatial_shapes, level_start_index,
                                    sampling_locations, attention_weights, out, out_dtype, N, S,
-                                   M, D, Lq, L, P, stream, nullptr, threshold);
+                                   M, D, Lq, L, P, query_order, stream, nullptr, threshold);
 }
 
 int msda_forward_fused(const void* value, int value_dtype, const int64_t* spatial_shapes,
                        const int64_t* level_start_index, const float* reference_points,
                        const float* sampling_offsets, const float* attention_logits, void* out,
                        int out_dtype, int64_t N, int64_t S, int64_t M, int64_t D, int64_t Lq,
-                       int64_t L, int64_t P, void* stream) {
+                       int64_t L, int64_t P, const int32_t* query_order, void* stream) {
     return forward<2, true>(value, value_dtype, spatial_shapes, level_start_index,
                             sampling_offsets, attention_logits, out, out_dtype, N, S, M, D, Lq,
-                            L, P, stream, reference_points);
+                            L, P, query_order, stream, reference_points);
 }
 
 int msda3d_forward_fused(const void* value, int value_dtype, const int64_t* spatial_shapes,
                          const int64_t* level_start_index, const float* reference_points,
                          const float* sampling_offsets, const float* attention_logits,
                          void* out, int out_dtype, int64_t N, int64_t S, int64_t M, int64_t D,
-                         int64_t Lq, int64_t L, int64_t P, void* stream) {
+                         int64_t Lq, int64_t L, int64_t P, const int32_t* query_order,
+                         void* stream) {
     return forward<3, true>(value, value_dtype, spatial_shapes, level_start_index,
                             sampling_offsets, attention_logits, out, out_dtype, N, S, M, D, Lq,
-                            L, P, stream, reference_points);
+                            L, P, query_order, stream, reference_points);
 }
 
 const char* msda_status_string(int status) {
@@ -333,7 +340,8 @@ const char* msda_status_string(int status) {
             return "misaligned pointer (value/out need 16 bytes, locations/weights 4, "
                    "shapes/starts 8)";
         case MSDA_ERR_OVERFLOW:
-            return "one image's value tensor is 2^31 bytes or larger (or S, M, Lq >= 2^31)";
+            return "one image's value tensor is 2^31 bytes or larger (or S, M, Lq >= 2^31; "
+                   "with a query order, also one image's locations or output gradient)";
         case MSDA_ERR_LAUNCH: return "HIP kernel launch failed";
         default: return "unknown status";
     }

@@ -279,7 +279,8 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
     const uint32_t q0 = (wave_id - slice * p.wps) * static_cast<uint32_t>(p.T);
     const uint32_t n = fast_div(slice, p.div_M);
     const uint32_t m = slice - n * static_cast<uint32_t>(p.M);
-    const uint32_t row0 = (n * static_cast<uint32_t>(p.Lq) + q0) * static_cast<uint32_t>(p.M) + m;
+    // the sample/gradient row of query q is (n*Lq + q)*M + m
+    const uint32_t image_q0 = n * static_cast<uint32_t>(p.Lq);
     const uint32_t ghead_base = n * gimage_bytes + m * ghead_bytes;
     const int G = 1 << p.log2G;
     float* gtile = gtile_all + wave * kTile;   // this wave's tiles' gradient rows
@@ -295,8 +296,8 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
         const bool live = wave_live && i < p.NI && s < p.LP &&
                           q0 + static_cast<uint32_t>(t) < static_cast<uint32_t>(p.nq);
         const int s_c = live ? s : 0;
-        const uint32_t sidx = row0 * static_cast<uint32_t>(p.LP) +
-                              static_cast<uint32_t>(t) * static_cast<uint32_t>(p.M * p.LP) +
+        const uint32_t qrow = image_q0 + query_at(p, q0 + static_cast<uint32_t>(t));
+        const uint32_t sidx = (qrow * static_cast<uint32_t>(p.M) + m) * static_cast<uint32_t>(p.LP) +
                               static_cast<uint32_t>(s_c);
         float xyz[DIM], a;
         load_sample<DIM>(p, live, sidx, xyz, a);
@@ -328,7 +329,8 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
     float gch[VEC];
     {
         const bool tile_live = wave_live && q0 + static_cast<uint32_t>(t) < static_cast<uint32_t>(p.nq);
-        const uint32_t row = row0 + static_cast<uint32_t>(t * p.M);
+        const uint32_t row =
+            (image_q0 + query_at(p, q0 + static_cast<uint32_t>(t))) * static_cast<uint32_t>(p.M) + m;
         const uint32_t goff = tile_live && chunk_live
                                   ? row * bp.gout_head_bytes + cc * (VEC * sizeof(TG))
                                   : kOutOfRange;

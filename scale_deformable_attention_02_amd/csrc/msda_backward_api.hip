@@ -78,7 +78,7 @@ int backward(const void* value, int value_dtype, const int64_t* spatial_shapes,
              const float* attention_weights, const void* grad_out, int grad_out_dtype,
              float* grad_value, float* grad_sampling_locations, float* grad_attention_weights,
              int64_t N, int64_t S, int64_t M, int64_t D, int64_t Lq, int64_t L, int64_t P,
-             void* stream) {
+             const int32_t* query_order, void* stream) {
     if (N < 0 || Lq < 0 || S < 1 || M < 1 || D < 1 || L < 1 || P < 1) return MSDA_ERR_DIM;
     if (!known_dtype(value_dtype) || !known_dtype(grad_out_dtype)) return MSDA_ERR_DTYPE;
     if (N == 0) return MSDA_OK;
@@ -94,7 +94,7 @@ int backward(const void* value, int value_dtype, const int64_t* spatial_shapes,
     if (head_bytes % 16 != 0 || head_bytes > 16 * msda::kWave) return MSDA_ERR_UNSUPPORTED;
     if (L > msda::kMaxLevels || L * P > msda::kMaxSamplesPerTile) return MSDA_ERR_UNSUPPORTED;
     if (!aligned(value, 16) || !aligned(grad_value, 16) || !aligned(spatial_shapes, 8) ||
-        !aligned(level_start_index, 8) ||
+        !aligned(level_start_index, 8) || !aligned(query_order, 4) ||
         (Lq > 0 && (!aligned(grad_out, 16) || !aligned(sampling_locations, 4) ||
                     !aligned(attention_weights, 4) || !aligned(grad_sampling_locations, 4) ||
                     !aligned(grad_attention_weights, 4))))
@@ -109,6 +109,12 @@ int backward(const void* value, int value_dtype, const int64_t* spatial_shapes,
     const int64_t image_bytes = S * M * head_bytes;
     const int64_t value_limit = elem == 2 ? kLimit / 2 : kLimit;
     if (gimage_bytes >= kLimit || image_bytes >= value_limit) return MSDA_ERR_OVERFLOW;
+
+    if (query_order && Lq > 0) {
+        const int64_t loc_q = M * L * P * DIM * 4, gout_q = M * gout_head_bytes;
+        const int64_t per_q = loc_q > gout_q ? loc_q : gout_q;
+        if (Lq * per_q >= kLimit || Lq * M >= (int64_t{1} << 30)) return MSDA_ERR_OVERFLOW;
+    }
 
     const hipStream_t hs = static_cast<hipStream_t>(stream);
     {
@@ -135,8 +141,11 @@ int backward(const void* value, int value_dtype, const int64_t* spatial_shapes,
     const int64_t gout_per_query = M * gout_head_bytes;
     const int64_t per_query = loc_per_query > gout_per_query ? loc_per_query : gout_per_query;
     const int64_t kTileLimit = int64_t{1} << 30;
+    // whole images per launch, else query ranges of one image (not with a
+    // visit order, whose positions address any query of the image)
+    const bool whole_images = Lq * per_query < kLimit && Lq * M < kTileLimit;
     int64_t nb = 0, nq = Lq;
-    if (Lq * per_query < kLimit && Lq * M < kTileLimit) {
+    if (whole_images) {
         nb = (value_limit - 1) / image_bytes;
         const int64_t by_grad = (kLimit - 1) / gimage_bytes;
         const int64_t by_rows = (kLimit - 1) / (Lq * per_query);
@@ -207,6 +216,7 @@ int backward(const void* value, int value_dtype, const int64_t* spatial_shapes,
             bp.gout_head_bytes = static_cast<uint32_t>(gout_head_bytes);
             bp.value_shift = elem == 2 ? 1u : 0u;
             bp.log2R = static_cast<uint32_t>(ceil_log2(D));
+            p.order = query_order;   // whole images: q0 == 0 and nquery == Lq
             launch_bwd<DIM>(value_dtype, grad_out_dtype, cpl, bp, hs);
             if (hipGetLastError() != hipSuccess) return MSDA_ERR_LAUNCH;
         }
@@ -223,11 +233,12 @@ int msda_backward(const void* value, int value_dtype, const int64_t* spatial_sha
                   const float* attention_weights, const void* grad_out, int grad_out_dtype,
                   float* grad_value, float* grad_sampling_locations,
                   float* grad_attention_weights, int64_t N, int64_t S, int64_t M, int64_t D,
-                  int64_t Lq, int64_t L, int64_t P, void* stream) {
+                  int64_t Lq, int64_t L, int64_t P, const int32_t* query_order,
+                  void* stream) {
     return backward<2>(value, value_dtype, spatial_shapes, level_start_index,
                        sampling_locations, attention_weights, grad_out, grad_out_dtype,
                        grad_value, grad_sampling_locations, grad_attention_weights, N, S, M, D,
-                       Lq, L, P, stream);
+                       Lq, L, P, query_order, stream);
 }
 
 int msda3d_backward(const void* value, int value_dtype, const int64_t* spatial_shapes,
@@ -235,11 +246,12 @@ int msda3d_backward(const void* value, int value_dtype, const int64_t* spatial_s
                     const float* attention_weights, const void* grad_out, int grad_out_dtype,
                     float* grad_value, float* grad_sampling_locations,
                     float* grad_attention_weights, int64_t N, int64_t S, int64_t M, int64_t D,
-                    int64_t Lq, int64_t L, int64_t P, void* stream) {
+                    int64_t Lq, int64_t L, int64_t P, const int32_t* query_order,
+                    void* stream) {
     return backward<3>(value, value_dtype, spatial_shapes, level_start_index,
                        sampling_locations, attention_weights, grad_out, grad_out_dtype,
                        grad_value, grad_sampling_locations, grad_attention_weights, N, S, M, D,
-                       Lq, L, P, stream);
+                       Lq, L, P, query_order, stream);
 }
 
 }  // extern "C"

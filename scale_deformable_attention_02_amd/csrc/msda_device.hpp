@@ -9,12 +9,14 @@
 //
 // Tile order.  A launch covers nb images x a range of nq queries, cut into
 // slices (n, m) of nq queries each, head-major.  Every wave takes T
-// consecutive queries of one slice (the last wave of a slice may run past nq:
-// those tiles are dead), so (n, m) is uniform per wave and lives in scalar
-// registers.  Consecutive workgroups - after the XCD renumbering below, the
-// whole stream of one XCD - walk one head's queries: the value rows they
-// gather are that head's D-channel slices, a footprint 1/M of the pyramid that
-// fits the XCD's L2.
+// consecutive positions of one slice (the last wave of a slice may run past
+// nq: those tiles are dead), so (n, m) is uniform per wave and lives in scalar
+// registers.  Position r is query r, or query order[r] when the caller gives
+// a visit order (one that puts queries sampling nearby pixels next to each
+// other raises the reuse of the rows below).  Consecutive workgroups - after
+// the XCD renumbering below, the whole stream of one XCD - walk one head's
+// queries: the value rows they gather are that head's D-channel slices, a
+// footprint 1/M of the pyramid that fits the XCD's L2.
 //
 // Work decomposition (per wave of 64 lanes):
 //   * The wave owns T consecutive tiles (same head, consecutive queries).
@@ -112,6 +114,9 @@ struct Params {
     uint32_t ref_bytes;
     // pruned forward only: samples with attention weight below this are dropped
     float prune;
+    // optional visit order, [nq] int32 (launches with an order cover whole
+    // images, so nq = Lq): position r of every slice takes query order[r]
+    const int32_t* order;
 };
 
 // One sample's contribution recipe: NC corner byte offsets (relative to the
@@ -303,6 +308,16 @@ __device__ __forceinline__ Slot<DIM == 2 ? 4 : 8> make_slot(const float (&xyz)[D
         sl.w[k] = ok ? (aw * wzk) * (wy[cy] * wx[cx]) : 0.0f;
     }
     return sl;
+}
+
+// The query visited at slice position pos (< nq + T): pos itself, or entry
+// pos of the caller's order, clamped to the image's queries so that no order
+// can address rows outside the tensors.  Past the end the order reads 0.
+__device__ __forceinline__ uint32_t query_at(const Params& p, uint32_t pos) {
+    if (p.order == nullptr) return pos;
+    const __amdgpu_buffer_rsrc_t r = buffer_of(p.order, static_cast<uint32_t>(p.nq) * 4u);
+    const uint32_t q = __builtin_amdgcn_raw_buffer_load_b32(r, pos * 4u, 0, 0);
+    return min(q, static_cast<uint32_t>(p.Lq - 1));
 }
 
 // Location and weight of one sample, index sidx of this launch (0 if !live:
@@ -524,8 +539,8 @@ __global__ __launch_bounds__(kBlockThreads) void msda_forward_kernel(Params p) {
     const uint32_t q0 = (wave_id - slice * p.wps) * static_cast<uint32_t>(p.T);
     const uint32_t n = fast_div(slice, p.div_M);
     const uint32_t m = slice - n * static_cast<uint32_t>(p.M);
-    // location/weight/output row of tile t is row0 + t*M
-    const uint32_t row0 = (n * static_cast<uint32_t>(p.Lq) + q0) * static_cast<uint32_t>(p.M) + m;
+    // the location/weight/output row of query q is (n*Lq + q)*M + m
+    const uint32_t image_q0 = n * static_cast<uint32_t>(p.Lq);
     const uint32_t head_base = n * p.image_bytes + m * p.head_bytes;
     const int G = 1 << p.log2G;
 
@@ -538,13 +553,12 @@ __global__ __launch_bounds__(kBlockThreads) void msda_forward_kernel(Params p) {
         const bool live = wave_live && i < p.NI && s < p.LP &&
                           q0 + static_cast<uint32_t>(t) < static_cast<uint32_t>(p.nq);
         const int s_c = live ? s : 0;
-        const uint32_t sidx = row0 * static_cast<uint32_t>(p.LP) +
-                              static_cast<uint32_t>(t) * static_cast<uint32_t>(p.M * p.LP) +
+        const uint32_t qrow = image_q0 + query_at(p, q0 + static_cast<uint32_t>(t));
+        const uint32_t sidx = (qrow * static_cast<uint32_t>(p.M) + m) * static_cast<uint32_t>(p.LP) +
                               static_cast<uint32_t>(s_c);
         float xyz[DIM], a;
         if constexpr (FUSED) {
             float ref[DIM];
-            const uint32_t qrow = n * static_cast<uint32_t>(p.Lq) + q0 + static_cast<uint32_t>(t);
             load_sample_fused<DIM>(p, live, sidx, qrow, xyz, a, ref);
             finish_sample_fused<DIM, ilog2<NG>()>(live, p.log2G, xyz, a, ref);
         } else {
@@ -576,6 +590,8 @@ __global__ __launch_bounds__(kBlockThreads) void msda_forward_kernel(Params p) {
     // lanes past the head's last chunk (D*size not a power-of-two multiple of
     // 16 bytes) re-read the last chunk and never store
     const uint32_t lane_off = static_cast<uint32_t>(min(c, p.nchunk - 1)) * 16u;
+    const uint32_t out_row =
+        (image_q0 + query_at(p, q0 + static_cast<uint32_t>(t))) * static_cast<uint32_t>(p.M) + m;
 
     float acc[VEC];
 #pragma unroll
@@ -585,8 +601,7 @@ __global__ __launch_bounds__(kBlockThreads) void msda_forward_kernel(Params p) {
 
     const bool store = j == 0 && c < p.nchunk && wave_live &&
                        q0 + static_cast<uint32_t>(t) < static_cast<uint32_t>(p.nq);
-    reduce_store<TO, CPL, VEC>(acc, G, store, p.out, row0 + static_cast<uint32_t>(t * p.M),
-                               p.out_head_bytes, c);
+    reduce_store<TO, CPL, VEC>(acc, G, store, p.out, out_row, p.out_head_bytes, c);
 }
 
 // ---------------------------------------------------------------------------
@@ -732,26 +747,29 @@ void msda_forward_staged_kernel(StagedParams sp) {
     const uint32_t stride = span * sp.wgs_per_slice;   // queries between this WG's chunks
     const uint32_t qa = k_in_slice * span;
     const uint32_t lp = static_cast<uint32_t>(p.LP);
-    const uint32_t lane_rel = static_cast<uint32_t>(ta) * static_cast<uint32_t>(p.M * p.LP) +
-                              static_cast<uint32_t>(sa < p.LP ? sa : 0);
+    const uint32_t lane_s = static_cast<uint32_t>(sa < p.LP ? sa : 0);
     const bool lane_has_sample = ia < NI && sa < p.LP;
+    const uint32_t image_q0 = n * static_cast<uint32_t>(p.Lq);
 
     // Locations and weights of the first chunk; each later chunk's are loaded
-    // one chunk ahead.
+    // one chunk ahead, and the query this lane loads them for (an entry of
+    // the visit order) two chunks ahead, so no location load waits for it.
     uint32_t q0 = qa + static_cast<uint32_t>(wave * p.T);
     float xyz[DIM], a, ref[DIM];
     const auto load = [&](uint32_t q, bool lv) {
-        const uint32_t qrow = n * static_cast<uint32_t>(p.Lq) + q;
-        const uint32_t sidx = (qrow * static_cast<uint32_t>(p.M) + m) * lp + lane_rel;
+        const uint32_t qrow = image_q0 + q;
+        const uint32_t sidx = (qrow * static_cast<uint32_t>(p.M) + m) * lp + lane_s;
         if constexpr (FUSED)
-            load_sample_fused<DIM>(p, lv, sidx, qrow + static_cast<uint32_t>(ta), xyz, a, ref);
+            load_sample_fused<DIM>(p, lv, sidx, qrow, xyz, a, ref);
         else
             load_sample<DIM>(p, lv, sidx, xyz, a);
     };
     bool live = lane_has_sample && q0 + static_cast<uint32_t>(ta) < qb;
-    load(q0, live);
+    load(query_at(p, q0 + static_cast<uint32_t>(ta)), live);
+    uint32_t q_next = query_at(p, q0 + stride + static_cast<uint32_t>(ta));
     for (uint32_t qc = qa; qc < qb; qc += stride) {
-        const uint32_t row0 = (n * static_cast<uint32_t>(p.Lq) + q0) * static_cast<uint32_t>(p.M) + m;
+        const uint32_t out_row =
+            (image_q0 + query_at(p, q0 + static_cast<uint32_t>(tb))) * static_cast<uint32_t>(p.M) + m;
 
         // ---- Phase A
         if constexpr (FUSED) finish_sample_fused<DIM, ilog2<NG>()>(live, p.log2G, xyz, a, ref);
@@ -772,7 +790,8 @@ void msda_forward_staged_kernel(StagedParams sp) {
         q0 += stride;
         if (qc + stride < qb) {
             live = lane_has_sample && q0 + static_cast<uint32_t>(ta) < qb;
-            load(q0, live);
+            load(q_next, live);
+            q_next = query_at(p, q0 + stride + static_cast<uint32_t>(ta));
         }
         wave_lds_sync();
 
@@ -785,8 +804,7 @@ void msda_forward_staged_kernel(StagedParams sp) {
         gather_lds<TV, NC, NG, VEC>(stage, my, hbm_end, lds_end, lane_off, acc);
 
         const bool store = jb == 0 && c < p.nchunk && q_this + static_cast<uint32_t>(tb) < qb;
-        reduce_store<TO, CPL, VEC>(acc, G, store, p.out, row0 + static_cast<uint32_t>(tb * p.M),
-                                   p.out_head_bytes, c);
+        reduce_store<TO, CPL, VEC>(acc, G, store, p.out, out_row, p.out_head_bytes, c);
         wave_lds_sync();
     }
 }

@@ -231,3 +231,47 @@ def test_linear_checks(lib):
     assert lcall(x=A + 8) == ALIGN and lcall(y=A + 2) == ALIGN and lcall(b=A + 2) == ALIGN
     assert lcall(N=1 << 20, K=1 << 11) == OVERFLOW
     assert lcall(R=0, x=0, w=0, y=0) == OK
+
+
+# ---- visit order: the order argument of the core entry points and the
+# order builder (host-side rejections only)
+
+def test_query_order_argument_checks(lib):
+    # misaligned order
+    assert raw_call(2, A, 0, A, A, A, A, A, 0, 1, 100, 8, 32, 10, 4, 4, 0, A + 2) == ALIGN
+    assert binding.raw_backward_call(2, A, 0, A, A, A, A, A, 0, A, A, A, 1, 100, 8, 32, 10,
+                                     4, 4, 0, A + 1) == ALIGN
+    assert binding.raw_fused_call(2, A, 0, A, A, A, A, A, A, 0, 1, 100, 8, 32, 10, 4, 4,
+                                  0, A + 2) == ALIGN
+    assert binding.raw_pruned_call(3, A, 0, A, A, A, A, 0.1, A, 0, 1, 100, 8, 32, 10, 4, 4,
+                                   0, A + 2) == ALIGN
+    # an order needs whole images per launch: one image's locations below
+    # 2^31 bytes (M*L*P*2*4 = 1024 bytes per query here)
+    big = 1 << 21
+    assert raw_call(2, A, 0, A, A, A, A, A, 0, 1, 100, 8, 32, big, 4, 4, 0, A) == OVERFLOW
+    assert binding.raw_backward_call(2, A, 0, A, A, A, A, A, 0, A, A, A, 1, 100, 8, 32, big,
+                                     4, 4, 0, A) == OVERFLOW
+
+
+def _shapes_array(shapes):
+    import numpy as np
+    arr = np.ascontiguousarray(np.array(shapes, dtype=np.int64))
+    return arr, arr.ctypes.data
+
+
+def test_query_order_builder_checks(lib):
+    arr, ptr = _shapes_array([[4, 4], [2, 2]])
+    call_order = binding.raw_query_order_call
+    assert call_order(0, 2, 2, 1, A, 20) == NULL
+    assert call_order(ptr, 2, 2, 1, 0, 20) == NULL
+    assert call_order(ptr, 2, 4, 1, A, 20) == DIM           # dims not 2 or 3
+    assert call_order(ptr, 0, 2, 1, A, 20) == DIM           # no levels
+    assert call_order(ptr, 2, 2, 1, A, 21) == DIM           # S is not the pixel total
+    assert call_order(ptr, 17, 2, 1, A, 20) == UNSUP        # L > 16
+    assert call_order(ptr, 2, 2, 1, A + 2, 20) == ALIGN
+    bad, bptr = _shapes_array([[4, 0], [2, 2]])
+    assert call_order(bptr, 2, 2, 1, A, 4) == DIM           # an empty level
+    wide, wptr = _shapes_array([[1, 1 << 20]])
+    assert call_order(wptr, 1, 2, 1, A, 1 << 20) == UNSUP   # extent >= 2^20
+    huge, hptr = _shapes_array([[1 << 19, 1 << 19]])
+    assert call_order(hptr, 1, 2, 0, A, 1 << 38) == OVERFLOW
