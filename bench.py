@@ -13,10 +13,10 @@ pipeline (torch softmax + add, then msda_forward) is timed beside it; with
 (the fraction of samples it drops and the unpruned kernel's time on the same
 inputs are reported beside it).
 Queries are visited in a Z-order (Morton) order of the pixels when the
-workload's queries are the pyramid's pixel centres (``--query-order``; the
-order depends only on the level shapes, so it is built once, before the timed
-steps, like any per-shape plan); every output is the same as in the raw
-query order, which ``--query-order none`` times.
+workload's queries are the pyramid's pixel centres, except in the 2D pruned
+forward (``--query-order``; the order depends only on the level shapes, so it
+is built once, before the timed steps, like any per-shape plan); every output
+is the same as in the raw query order, which ``--query-order none`` times.
 Steps cycle over several distinct copies of the inputs whose total exceeds
 twice the 256 MB Infinity Cache, so each step reads its inputs from HBM
 rather than from a cache warmed by the previous step.
@@ -339,7 +339,8 @@ def main(argv=None):
                     default="auto",
                     help="visit order of the queries: a Z-order of the pixels with the "
                          "levels interleaved or level by level, or none (the raw order); "
-                         "auto = interleaved for pixel-centre workloads, else none")
+                         "auto = interleaved for pixel-centre workloads (except the 2D "
+                         "pruned forward), else none")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip timing the oracle (for profiler runs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -387,23 +388,23 @@ def main(argv=None):
 
     order_kind = args.query_order
     if order_kind == "auto":
-        order_kind = "interleaved" if w.queries == "pixel_centres" else "none"
+        # the measured best: the interleaved Z-order for pixel-centre queries,
+        # except the 2D pruned forward, which runs slower with it
+        best = w.queries == "pixel_centres" and not (pruned and w.dims == 2)
+        order_kind = "interleaved" if best else "none"
     if order_kind != "none" and w.queries != "pixel_centres":
         print(f"bench.py: --query-order {order_kind} needs pixel-centre queries; "
               f"{w.name} has {w.queries!r}", file=sys.stderr)
         return 2
     order, order_build_us = None, None
     if order_kind != "none":
-        # built once per pyramid shape; the second build is timed (the first
-        # also loads the kernel's code object)
+        # built once per pyramid shape, before the timed steps; its GPU time is
+        # reported (mean of back-to-back rebuilds, host overhead excluded)
         order = msda_query_order(w.shapes, order_kind == "levels", device=dev)
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        msda_query_order(w.shapes, order_kind == "levels", out=order)
-        e1.record()
-        torch.cuda.synchronize()
-        order_build_us = e0.elapsed_time(e1) * 1e3
+        order_build_us = launch_times(
+            lambda i: msda_query_order(w.shapes, order_kind == "levels", out=order), 10,
+            torch.cuda.current_stream(dev), 200.0) * 1e6
     if backward:
         outs = [(torch.empty_like(d["value"], dtype=torch.float32),
                  torch.empty_like(d["sampling_locations"]),
