@@ -166,6 +166,30 @@ __device__ __forceinline__ uint32_t div_small(uint32_t x, uint32_t d, float rcp)
     return q;
 }
 
+// One lane's value moved across lanes by a DPP control inside the VALU (no
+// LDS-crossbar permute).  Every control used here reads a lane of the same
+// row of 16, so all sources are valid.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over each run of CPL consecutive lanes (CPL a power of two), the same
+// butterfly as x += x[lane ^ s] for s = 1, 2, 4, ... and bit-identical to it:
+// the xor-1 and xor-2 steps are quad permutations; after them every lane of a
+// quad holds the same bits (fp addition commutes), so mirroring within 8 lanes
+// and then within 16 reads a lane holding exactly what xor 4 and xor 8 would.
+template <int CPL>
+__device__ __forceinline__ float lane_group_sum(float x) {
+    if constexpr (CPL >= 2) x += dpp_move<0xB1>(x);    // quad_perm [1,0,3,2]
+    if constexpr (CPL >= 4) x += dpp_move<0x4E>(x);    // quad_perm [2,3,0,1]
+    if constexpr (CPL >= 8) x += dpp_move<0x141>(x);   // row_half_mirror
+    if constexpr (CPL >= 16) x += dpp_move<0x140>(x);  // row_mirror
+    if constexpr (CPL >= 32) x += __shfl_xor(x, 16, kWave);
+    if constexpr (CPL >= 64) x += __shfl_xor(x, 32, kWave);
+    return x;
+}
+
 template <int SLOTS>
 struct DedupShared {
     // two windows per level (x < W/2, x >= W/2), window w = 2 * level + side
@@ -361,8 +385,7 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
         }
         // sum the CPL lanes' partial dots of this group
 #pragma unroll
-        for (int k = 0; k < NC; ++k)
-            for (int s = 1; s < CPL; s <<= 1) dot[k] += __shfl_xor(dot[k], s, kWave);
+        for (int k = 0; k < NC; ++k) dot[k] = lane_group_sum<CPL>(dot[k]);
 
         if (c == 0 && sl.sidx != kNoSample) {
             // d x_hat / d x = W (, H, Z) of the sample's level
