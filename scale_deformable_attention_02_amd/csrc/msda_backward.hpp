@@ -166,14 +166,6 @@ __device__ __forceinline__ uint32_t div_small(uint32_t x, uint32_t d, float rcp)
     return q;
 }
 
-// One lane's value moved across lanes by a DPP control inside the VALU (no
-// LDS-crossbar permute).  Every control used here reads a lane of the same
-// row of 16, so all sources are valid.
-template <int CTRL>
-__device__ __forceinline__ float dpp_move(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-
 // Sum over each run of CPL consecutive lanes (CPL a power of two), the same
 // butterfly as x += x[lane ^ s] for s = 1, 2, 4, ... and bit-identical to it:
 // the xor-1 and xor-2 steps are quad permutations; after them every lane of a

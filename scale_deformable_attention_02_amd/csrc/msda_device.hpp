@@ -446,14 +446,41 @@ __device__ __forceinline__ void gather_lds(const unsigned char* stage, const Slo
     }
 }
 
+// One lane's value moved across lanes by a DPP control inside the VALU (no
+// LDS-crossbar permute).  Every control used here reads a lane of the same
+// row of 16, so all sources are valid.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// acc[e] += acc[e] of the lane S further on in its row of 16 (0 < S < 16):
+// rotating a row right by 16 - S brings lane i + S (mod 16) to lane i.
+template <int S, int VEC>
+__device__ __forceinline__ void add_rotated(float (&acc)[VEC]) {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] += dpp_move<0x120 + (16 - S)>(acc[e]);   // row_ror
+}
+
 // Sum the G point groups of each tile (lanes CPL apart) and store the lanes of
-// the first group.
+// the first group.  A tile's lanes are G*CPL consecutive lanes; within a row
+// of 16, each step adds the lane s further on (a row rotation in the VALU add),
+// which gives the first group's lanes the same operands in the same order as
+// the butterfly x += x[lane ^ s]; wider steps use lane permutes.
 template <typename TO, int CPL, int VEC>
 __device__ __forceinline__ void reduce_store(float (&acc)[VEC], int G, bool store, void* out,
                                              uint32_t row, uint32_t out_head_bytes, int c) {
     for (int s = CPL; s < CPL * G; s <<= 1) {
+        switch (s) {
+            case 1: add_rotated<1, VEC>(acc); break;
+            case 2: add_rotated<2, VEC>(acc); break;
+            case 4: add_rotated<4, VEC>(acc); break;
+            case 8: add_rotated<8, VEC>(acc); break;
+            default:
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[e] += __shfl_xor(acc[e], s, kWave);
+                for (int e = 0; e < VEC; ++e) acc[e] += __shfl_xor(acc[e], s, kWave);
+                break;
+        }
     }
     if (store) {
         char* dst = static_cast<char*>(out) + static_cast<size_t>(row) * out_head_bytes +
