@@ -264,7 +264,7 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
     __shared__ LevelGeom smeta[kMaxSamplesPerTile];
     __shared__ BwdSlot<NC, DIM> slots[WAVES][kWave];
     constexpr int kTile = grad_tile_floats<DIM, DEDUP>();
-    __shared__ float gtile_all[WAVES * kTile];
+    __shared__ __align__(16) float gtile_all[WAVES * kTile];
     using DedupT = typename std::conditional<DEDUP, DedupShared<kDedupSlots>, int>::type;
     __shared__ DedupT dd;
 
@@ -632,12 +632,20 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
         }
         __syncthreads();
         // D5: window by window, groups of R lanes take every ngroups-th pixel
-        // (non-empty pixel in 3D)
-        const int rl = 1 << log2R;               // lanes per row (D <= 64)
+        // (non-empty pixel in 3D).  Lane (c4, es) of a group adds channels
+        // 4*c4 .. 4*c4+3 of entries es, es+4, es+8, ... of the pixel's list
+        // (one 16-byte LDS read per entry and lane); the four entry subsets
+        // are summed across lanes, and lane (c4, es) then adds channel
+        // 4*c4 + es of the total: one atomic per channel, the R lanes of a
+        // group covering one contiguous row.
+        const int rl = 1 << log2R;               // lanes per row (4 <= R <= 64)
         const int ngroups = kThreads / rl;
         const int grp = tid / rl, ch = tid % rl;
-        // lanes past D (D not a power of two) read channel D-1 and never store
-        const uint32_t chc = static_cast<uint32_t>(min(ch, D - 1));
+        const int q4 = rl >> 2;                  // lanes per entry subset
+        const int c4 = ch & (q4 - 1), es = ch / q4;
+        const int chan = 4 * c4 + es;
+        // lanes past D (D not a power of two) read the last chunk and never store
+        const uint32_t c4c = 4u * static_cast<uint32_t>(min(c4, D / 4 - 1));
         const float* gflat = gtile_all;
         const int nnz_all = dd.nnz;
         const uint32_t total_all = dd.total;
@@ -662,26 +670,39 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
                     b1 = dd.offs[base + idx + 1];
                     if (b0 == b1) continue;
                 }
-                // four entries per round: their eight LDS reads overlap
-                float acc0 = 0.0f, acc1 = 0.0f;
-                uint32_t e = b0;
-                for (; e + 4u <= b1; e += 4u) {
-                    DedupEntry en[4];
-                    float gv[4];
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) en[u] = list[e + u];
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) gv[u] = gflat[en[u].gi + chc];
-                    acc0 = fmaf(en[0].aw, gv[0], acc0);
-                    acc1 = fmaf(en[1].aw, gv[1], acc1);
-                    acc0 = fmaf(en[2].aw, gv[2], acc0);
-                    acc1 = fmaf(en[3].aw, gv[3], acc1);
+                // two entries per lane and round (eight per group)
+                float a0[4] = {0.0f, 0.0f, 0.0f, 0.0f}, a1[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                uint32_t e = b0 + static_cast<uint32_t>(es);
+                for (; e + 4u < b1; e += 8u) {
+                    const DedupEntry en0 = list[e], en1 = list[e + 4u];
+                    const float4 g0 = *reinterpret_cast<const float4*>(gflat + en0.gi + c4c);
+                    const float4 g1 = *reinterpret_cast<const float4*>(gflat + en1.gi + c4c);
+                    a0[0] = fmaf(en0.aw, g0.x, a0[0]);
+                    a0[1] = fmaf(en0.aw, g0.y, a0[1]);
+                    a0[2] = fmaf(en0.aw, g0.z, a0[2]);
+                    a0[3] = fmaf(en0.aw, g0.w, a0[3]);
+                    a1[0] = fmaf(en1.aw, g1.x, a1[0]);
+                    a1[1] = fmaf(en1.aw, g1.y, a1[1]);
+                    a1[2] = fmaf(en1.aw, g1.z, a1[2]);
+                    a1[3] = fmaf(en1.aw, g1.w, a1[3]);
                 }
-                for (; e < b1; ++e) {
-                    const DedupEntry en = list[e];
-                    acc0 = fmaf(en.aw, gflat[en.gi + chc], acc0);
+                if (e < b1) {
+                    const DedupEntry en0 = list[e];
+                    const float4 g0 = *reinterpret_cast<const float4*>(gflat + en0.gi + c4c);
+                    a0[0] = fmaf(en0.aw, g0.x, a0[0]);
+                    a0[1] = fmaf(en0.aw, g0.y, a0[1]);
+                    a0[2] = fmaf(en0.aw, g0.z, a0[2]);
+                    a0[3] = fmaf(en0.aw, g0.w, a0[3]);
                 }
-                const float acc = acc0 + acc1;
+                // sum the four entry subsets (lanes q4 and 2*q4 apart)
+                float tot[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    tot[u] = a0[u] + a1[u];
+                    tot[u] += __shfl_xor(tot[u], q4, kWave);
+                    tot[u] += __shfl_xor(tot[u], 2 * q4, kWave);
+                }
+                const float acc = es == 0 ? tot[0] : es == 1 ? tot[1] : es == 2 ? tot[2] : tot[3];
                 // window slot -> (z, y, x) of the level (z = 0 in 2D)
                 const uint32_t zy = div_small(static_cast<uint32_t>(local), static_cast<uint32_t>(ww), rw);
                 const uint32_t x = static_cast<uint32_t>(local) - zy * static_cast<uint32_t>(ww);
@@ -691,9 +712,9 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
                                       static_cast<uint32_t>(oy) + y) * static_cast<uint32_t>(lg.W) +
                                      static_cast<uint32_t>(ox) + x;
                 const uint32_t off = ghead_base + lg.start_bytes + pix * grow_bytes;
-                if (ch < D)
+                if (chan < D)
                     __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(
-                        acc, rgv, off + 4u * static_cast<uint32_t>(ch), 0, 0);
+                        acc, rgv, off + 4u * static_cast<uint32_t>(chan), 0, 0);
             }
         }
     }
