@@ -209,3 +209,46 @@ def test_empty_queries_with_an_order():
     out = msda_forward(d["value"], d["spatial_shapes"], d["level_start_index"],
                        d["sampling_locations"], d["attention_weights"], query_order=order)
     assert out.shape == (2, 0, 16)
+
+
+@pytest.mark.parametrize("name", ["detr_encoder", "detr_encoder_bf16_b8", "volume3d"])
+def test_full_size_workloads_in_the_bench_order(name):
+    # the launch configuration the benchmark times: the full workload visited
+    # in the interleaved Z-order.  Forward, fused forward and the location and
+    # weight gradients bitwise against the raw order; forward rows sampled and
+    # grad_value in full against the oracle.
+    w = CONFIGS[name]
+    dims = w.dims
+    inp = make_inputs(w)
+    d = _to_dev(inp)
+    order = msda_query_order(w.shapes, False, device=DEV)
+    fwd = msda_forward if dims == 2 else msda3d_forward
+    fused = msda_forward_fused if dims == 2 else msda3d_forward_fused
+    bwd = msda_backward if dims == 2 else msda3d_backward
+    args = (d["value"], d["spatial_shapes"], d["level_start_index"], d["sampling_locations"],
+            d["attention_weights"])
+    _log(f"[order] full size {name}: forward")
+    base = fwd(*args)
+    got = fwd(*args, query_order=order)
+    torch.cuda.synchronize()
+    assert torch.equal(got, base)
+    rows = torch.randperm(w.queries_per_image, generator=torch.Generator().manual_seed(9))[:48]
+    sub = dict(inp, sampling_locations=inp["sampling_locations"][:, rows].contiguous(),
+               attention_weights=inp["attention_weights"][:, rows].contiguous())
+    assert_parity(got[:, rows.to(DEV)], oracle_fwd(dims, sub))
+    _log(f"[order] full size {name}: fused forward")
+    fin = _to_dev(make_fused_inputs(w))
+    fargs = (fin["value"], fin["spatial_shapes"], fin["level_start_index"],
+             fin["reference_points"], fin["sampling_offsets"], fin["attention_logits"])
+    fb = fused(*fargs)
+    fo = fused(*fargs, query_order=order)
+    torch.cuda.synchronize()
+    assert torch.equal(fo, fb)
+    _log(f"[order] full size {name}: backward")
+    grad = make_grad_out(w)
+    g = grad.to(DEV)
+    _, gl0, ga0 = bwd(*args, g)
+    gv, gl, ga = bwd(*args, g, query_order=order)
+    torch.cuda.synchronize()
+    assert torch.equal(gl, gl0) and torch.equal(ga, ga0)
+    check_backward(dims, inp, grad, (gv, gl, ga))
