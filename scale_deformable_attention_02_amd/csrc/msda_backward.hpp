@@ -177,8 +177,8 @@ __device__ __forceinline__ float lane_group_sum(float x) {
     if constexpr (CPL >= 4) x += dpp_move<0x4E>(x);    // quad_perm [2,3,0,1]
     if constexpr (CPL >= 8) x += dpp_move<0x141>(x);   // row_half_mirror
     if constexpr (CPL >= 16) x += dpp_move<0x140>(x);  // row_mirror
-    if constexpr (CPL >= 32) x += __shfl_xor(x, 16, kWave);
-    if constexpr (CPL >= 64) x += __shfl_xor(x, 32, kWave);
+    if constexpr (CPL >= 32) x = xor_combine(x, 16, AddOp());
+    if constexpr (CPL >= 64) x = xor_combine(x, 32, AddOp());
     return x;
 }
 

@@ -366,6 +366,47 @@ __device__ __forceinline__ void load_sample_fused(const Params& p, bool live, ui
     if (!live) a = -__builtin_inff();
 }
 
+// One lane's value moved across lanes by a DPP control inside the VALU (no
+// LDS-crossbar permute).  Every control used here reads a lane of the same
+// row of 16, so all sources are valid.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// op(x, x[lane ^ s]) on every lane, s a power of two below 64, for a
+// commutative op (+, fmaxf): the butterfly step, bit for bit.  The lane moves
+// stay in the VALU where the hardware has one: quad permutations (s = 1, 2), a
+// row of 16 rotated by 8 (s = 8), and the row-pair swaps, which hand every
+// lane both values of its pair, lower lane first (s = 16, 32).  s = 4 uses an
+// LDS-crossbar permute.
+template <typename Op>
+__device__ __forceinline__ float xor_combine(float x, int s, Op op) {
+    switch (s) {
+        case 1: return op(x, dpp_move<0xB1>(x));    // quad_perm [1,0,3,2]
+        case 2: return op(x, dpp_move<0x4E>(x));    // quad_perm [2,3,0,1]
+        case 8: return op(x, dpp_move<0x128>(x));   // row_ror:8
+        case 16: {
+            const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                            false, false);
+            return op(__uint_as_float(p[0]), __uint_as_float(p[1]));
+        }
+        case 32: {
+            const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                            false, false);
+            return op(__uint_as_float(p[0]), __uint_as_float(p[1]));
+        }
+        default: return op(x, __shfl_xor(x, s, kWave));
+    }
+}
+
+struct AddOp {
+    __device__ __forceinline__ float operator()(float a, float b) const { return a + b; }
+};
+struct MaxOp {
+    __device__ __forceinline__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+
 // Fused front end, finish step: location = reference point + offset (one fp32
 // add per coordinate), and the attention weight = softmax of the logits over
 // the tile's L*P samples.  The lanes of one tile differ only in the bits below
@@ -377,14 +418,14 @@ __device__ __forceinline__ void finish_sample_fused(bool live, int log2G, float 
 #pragma unroll
     for (int d = 0; d < DIM; ++d) xyz[d] = ref[d] + xyz[d];
     float mx = a;
-    for (int b = 0; b < log2G; ++b) mx = fmaxf(mx, __shfl_xor(mx, 1 << b, kWave));
+    for (int b = 0; b < log2G; ++b) mx = xor_combine(mx, 1 << b, MaxOp());
 #pragma unroll
-    for (int b = LOG2NG; b < 6; ++b) mx = fmaxf(mx, __shfl_xor(mx, 1 << b, kWave));
+    for (int b = LOG2NG; b < 6; ++b) mx = xor_combine(mx, 1 << b, MaxOp());
     const float e = live ? expf(a - mx) : 0.0f;
     float sum = e;
-    for (int b = 0; b < log2G; ++b) sum += __shfl_xor(sum, 1 << b, kWave);
+    for (int b = 0; b < log2G; ++b) sum = xor_combine(sum, 1 << b, AddOp());
 #pragma unroll
-    for (int b = LOG2NG; b < 6; ++b) sum += __shfl_xor(sum, 1 << b, kWave);
+    for (int b = LOG2NG; b < 6; ++b) sum = xor_combine(sum, 1 << b, AddOp());
     a = live ? e / sum : 0.0f;
 }
 
@@ -446,14 +487,6 @@ __device__ __forceinline__ void gather_lds(const unsigned char* stage, const Slo
     }
 }
 
-// One lane's value moved across lanes by a DPP control inside the VALU (no
-// LDS-crossbar permute).  Every control used here reads a lane of the same
-// row of 16, so all sources are valid.
-template <int CTRL>
-__device__ __forceinline__ float dpp_move(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-
 // acc[e] += acc[e] of the lane S further on in its row of 16 (0 < S < 16):
 // rotating a row right by 16 - S brings lane i + S (mod 16) to lane i.
 template <int S, int VEC>
@@ -478,7 +511,7 @@ __device__ __forceinline__ void reduce_store(float (&acc)[VEC], int G, bool stor
             case 8: add_rotated<8, VEC>(acc); break;
             default:
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) acc[e] += __shfl_xor(acc[e], s, kWave);
+                for (int e = 0; e < VEC; ++e) acc[e] = xor_combine(acc[e], s, AddOp());
                 break;
         }
     }
