@@ -158,11 +158,12 @@ constexpr int dedup_slots() { return DIM == 2 ? 3072 : 8192; }
 
 // floor(x / d) for x < 2^24, d >= 1, from rcp = 1.0f / d: x * rcp is within
 // one of x / d (both exact below 2^24, rcp within 2^-24 relative), so one
-// correction step makes it exact.
+// correction step makes it exact.  The two corrections exclude each other
+// (after a decrement (q+1)*d is the old q*d > x), so both are plain selects.
 __device__ __forceinline__ uint32_t div_small(uint32_t x, uint32_t d, float rcp) {
     uint32_t q = static_cast<uint32_t>(static_cast<float>(x) * rcp);
-    if (q * d > x) --q;
-    else if ((q + 1u) * d <= x) ++q;
+    q = q * d > x ? q - 1u : q;
+    q = (q + 1u) * d <= x ? q + 1u : q;
     return q;
 }
 
@@ -702,7 +703,10 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
                     tot[u] += __shfl_xor(tot[u], q4, kWave);
                     tot[u] += __shfl_xor(tot[u], 2 * q4, kWave);
                 }
-                const float acc = es == 0 ? tot[0] : es == 1 ? tot[1] : es == 2 ? tot[2] : tot[3];
+                // channel 4*c4 + es of the total, picked by the bits of es
+                const float lo = (es & 1) ? tot[1] : tot[0];
+                const float hi = (es & 1) ? tot[3] : tot[2];
+                const float acc = (es & 2) ? hi : lo;
                 // window slot -> (z, y, x) of the level (z = 0 in 2D)
                 const uint32_t zy = div_small(static_cast<uint32_t>(local), static_cast<uint32_t>(ww), rw);
                 const uint32_t x = static_cast<uint32_t>(local) - zy * static_cast<uint32_t>(ww);
