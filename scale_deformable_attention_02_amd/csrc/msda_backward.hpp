@@ -359,6 +359,12 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
     }
 
     const BwdSlot<NC, DIM>* my = &slots[wave][g];
+    // the first lane of each point group stores the sample's location and
+    // weight gradients; the other lanes' stores get an out-of-range offset,
+    // which the buffer store drops (no branch around the stores)
+    const __amdgpu_buffer_rsrc_t rgl = buffer_of(bp.grad_loc, p.loc_bytes);
+    const __amdgpu_buffer_rsrc_t rga = buffer_of(bp.grad_attw, p.attw_bytes);
+#pragma unroll 2
     for (int i = 0; i < p.NI; ++i) {
         const BwdSlot<NC, DIM> sl = my[i * NG];
         float dot[NC];
@@ -380,7 +386,8 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
 #pragma unroll
         for (int k = 0; k < NC; ++k) dot[k] = lane_group_sum<CPL>(dot[k]);
 
-        if (c == 0 && sl.sidx != kNoSample) {
+        {
+            const bool store = c == 0 && sl.sidx != kNoSample;
             // d x_hat / d x = W (, H, Z) of the sample's level
             const LevelGeom lgs = smeta[min(i * G + (g & (G - 1)), p.LP - 1)];
             const float ext[3] = {static_cast<float>(lgs.W), static_cast<float>(lgs.H),
@@ -417,9 +424,17 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
                 for (int d = 0; d < 3; ++d) gl[d] = sl.a * ext[d] * g3[d];
             }
             // a sample outside the support has a = 0 and all weights 0: zeros
-            bp.grad_attw[sl.sidx] = da;
-#pragma unroll
-            for (int d = 0; d < DIM; ++d) bp.grad_loc[static_cast<size_t>(sl.sidx) * DIM + d] = gl[d];
+            const uint32_t oa = store ? sl.sidx * 4u : kOutOfRange;
+            const uint32_t ol = store ? sl.sidx * (DIM * 4u) : kOutOfRange;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(da), rga, oa, 0, 0);
+            if constexpr (DIM == 2) {
+                const u32x2 v = {__float_as_uint(gl[0]), __float_as_uint(gl[1])};
+                __builtin_amdgcn_raw_buffer_store_b64(v, rgl, ol, 0, 0);
+            } else {
+                const u32x3 v = {__float_as_uint(gl[0]), __float_as_uint(gl[1]),
+                                 __float_as_uint(gl[2])};
+                __builtin_amdgcn_raw_buffer_store_b96(v, rgl, ol, 0, 0);
+            }
         }
     }
 

@@ -189,6 +189,7 @@ struct OutTraits;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 
 template <typename V>
 __device__ __forceinline__ void store_out(V* dst, V v) {
