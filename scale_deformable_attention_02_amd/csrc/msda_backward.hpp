@@ -446,6 +446,7 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
     // collect their contributions per pixel; the other corners keep the
     // direct atomics of phase C.
     uint32_t slot_id[NC], pos[NC];   // D2's table slot and list place of each corner
+    bool wave_direct = true;         // phase C has corners to add in this wave
     if constexpr (DEDUP) {
         // each lane widens its own level's boxes (LDS integer atomics; the
         // minima as maxima of complements)
@@ -514,22 +515,31 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
 
         // D2: each windowed corner takes a place in its pixel's list (LDS
         // integer atomics; counts stay below 2^16, at most WAVES * 64 * NC
-        // entries) and leaves phase C (its offset in the slot is cleared)
+        // entries) and leaves phase C (its offset in the slot is cleared).
+        // Branch-free: every lane issues its NC atomics; a corner outside the
+        // windows adds 0 to a table word picked by lane and corner (no count
+        // changes, and no pile-up on one address).
+        bool direct = false;   // a corner of this sample stays in phase C
 #pragma unroll
         for (int k = 0; k < NC; ++k) {
-            slot_id[k] = 0xffffffffu;
-            pos[k] = 0u;
             const int cx = k & 1, cy = (k >> 1) & 1, cz = k >> 2;
             const int x = my_x0 + cx;
             const int w = 2 * my_level + (x >= half ? 1 : 0);
-            if (my_in && mine.off[k] != kOutOfRange && dd.base[w] >= 0) {
-                const int lx = x - dd.ox[w], ly = my_y0 + cy - dd.oy[w], lz = my_z0 + cz - dd.oz[w];
-                slot_id[k] = static_cast<uint32_t>(dd.base[w] + (lz * dd.hh[w] + ly) * dd.ww[w] + lx);
-                const uint32_t sh = (slot_id[k] & 1u) * 16u;
-                pos[k] = (atomicAdd(&dd.count2[slot_id[k] >> 1], 1u << sh) >> sh) & 0xffffu;
-                slots[wave][lane].off[k] = kOutOfRange;
-            }
+            const int base_w = dd.base[w];
+            const bool corner = my_in && mine.off[k] != kOutOfRange;
+            const bool windowed = corner && base_w >= 0;
+            direct = direct || (corner && base_w < 0);
+            const int lx = x - dd.ox[w], ly = my_y0 + cy - dd.oy[w], lz = my_z0 + cz - dd.oz[w];
+            const uint32_t sid =
+                windowed ? static_cast<uint32_t>(base_w + (lz * dd.hh[w] + ly) * dd.ww[w] + lx)
+                         : static_cast<uint32_t>(2 * (lane * NC + k)) % kDedupSlots;
+            slot_id[k] = windowed ? sid : 0xffffffffu;
+            const uint32_t sh = (sid & 1u) * 16u;
+            pos[k] = (atomicAdd(&dd.count2[sid >> 1], windowed ? 1u << sh : 0u) >> sh) & 0xffffu;
+            if (windowed) mine.off[k] = kOutOfRange;
         }
+        slots[wave][lane] = mine;
+        wave_direct = __ballot(direct) != 0ull;
     }
 
     // ---- Phase C: grad_value[row_c][d] += A * w_c * g[t][d] over the flat
@@ -543,7 +553,8 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
     const uint32_t rmask = (1u << log2R) - 1u;
     uint32_t total = static_cast<uint32_t>(p.NI * NG) << (log2R + kLog2NC);
     if constexpr (DEDUP) {
-        if (!dd.any_direct) total = 0u;   // every contribution goes through phase D
+        // every contribution goes through phase D (in the workgroup, or this wave)
+        if (!dd.any_direct || !wave_direct) total = 0u;
     }
     const int log2G = p.log2G;
     for (uint32_t f = static_cast<uint32_t>(lane); f < total; f += kWave) {
