@@ -170,10 +170,13 @@ def launch_times(step, n, stream, host_us_per_step):
     return a.elapsed_time(b) / 1e3 / n
 
 
-def cpu_baseline(w, inp, max_points=60_000_000, grad_out=None, threshold=None):
-    """Time the oracle (single-threaded C) on the same inputs, bounded; the
-    backward oracle when ``grad_out`` is given, the fused-front-end oracle when
-    ``inp`` holds reference points, offsets and logits."""
+def cpu_baseline(w, inp, max_points=60_000_000, grad_out=None, threshold=None,
+                 min_seconds=10.0, max_passes=200):
+    """Time the oracle (single-threaded C) on the same inputs, bounded: at most
+    ``max_points`` sampled points per pass, passes repeated until
+    ``min_seconds`` have elapsed (or ``max_passes``).  The backward oracle when
+    ``grad_out`` is given, the fused-front-end oracle when ``inp`` holds
+    reference points, offsets and logits."""
     import numpy as np
 
     import oracle
@@ -212,17 +215,23 @@ def cpu_baseline(w, inp, max_points=60_000_000, grad_out=None, threshold=None):
         args += (grad_out[:nb, :nq].double().numpy(),)
     if threshold is not None:
         args += (threshold,)
+    passes = 0
     t0 = time.perf_counter()
-    fn(*args)
-    dt = time.perf_counter() - t0
-    points = nb * nq * per_query
+    while True:
+        fn(*args)
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds or passes >= max_passes:
+            break
+    points = nb * nq * per_query * passes
     return {
         "value": points / dt,
         "unit": "sampled points/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"{sample}: {points} sampled points in {dt:.2f} s, single-threaded C "
-                  f"oracle (fp64 accumulate) on {platform.processor() or platform.machine()}",
+        "sample": f"{sample}, {passes} passes: {points} sampled points in {dt:.2f} s, "
+                  f"single-threaded C oracle (fp64 accumulate) on "
+                  f"{platform.processor() or platform.machine()}",
     }
 
 
