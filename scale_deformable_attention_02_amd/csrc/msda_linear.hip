@@ -376,11 +376,14 @@ __global__ __launch_bounds__(kThreads) void linear_bf16_kernel(LinearParams p) {
     store_tiles<TY>(p, row0, col0, am, bn, lane, acc);
 }
 
-// fp32 operands: register-staged, double-buffered LDS.
+// fp32 operands: register-staged, one LDS buffer.  The next K step's tiles
+// are loaded into registers while the MFMAs read the current ones, and stored
+// after a barrier; with 37 KB of LDS four workgroups share a CU, which fills
+// the GPU in fewer rounds than two double-buffered ones.
 template <typename TY>
 __global__ __launch_bounds__(kThreads) void linear_f32_kernel(LinearParams p) {
     constexpr int kTileBytes = 128 * kF32Stride;
-    __shared__ __align__(16) unsigned char lds[2][2][kTileBytes];   // [stage][X, W]
+    __shared__ __align__(16) unsigned char lds[2][kTileBytes];   // [X, W]
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const uint32_t blk = msda::xcd_contiguous_block(blockIdx.x, p.num_blocks);
@@ -401,24 +404,24 @@ __global__ __launch_bounds__(kThreads) void linear_f32_kernel(LinearParams p) {
     uint32_t bx[F32Tile::kChunks][4], bw[F32Tile::kChunks][4];
     F32Tile::load(rx, row0, rows_x, 0, K, tid, bx);
     F32Tile::load(rw, col0, rows_w, 0, K, tid, bw);
-    F32Tile::store(lds[0][0], tid, bx);
-    F32Tile::store(lds[0][1], tid, bw);
+    F32Tile::store(lds[0], tid, bx);
+    F32Tile::store(lds[1], tid, bw);
     __syncthreads();
 
     const int steps = p.K / kBK;
     for (int s = 0; s < steps; ++s) {
-        const int cur = s & 1;
         const bool more = s + 1 < steps;
         if (more) {
             F32Tile::load(rx, row0, rows_x, (s + 1) * kBK, K, tid, bx);
             F32Tile::load(rw, col0, rows_w, (s + 1) * kBK, K, tid, bw);
         }
-        mma_step_f32(lds[cur][0], lds[cur][1], am, bn, lane, acc);
+        mma_step_f32(lds[0], lds[1], am, bn, lane, acc);
         if (more) {
-            F32Tile::store(lds[cur ^ 1][0], tid, bx);
-            F32Tile::store(lds[cur ^ 1][1], tid, bw);
+            __syncthreads();   // every wave has read this step's tiles
+            F32Tile::store(lds[0], tid, bx);
+            F32Tile::store(lds[1], tid, bw);
+            __syncthreads();
         }
-        __syncthreads();
     }
 
     store_tiles<TY>(p, row0, col0, am, bn, lane, acc);
