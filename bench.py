@@ -139,6 +139,19 @@ def counters_for(workload_name: str, op: str = "forward", query_order: str = "no
     return entry.get("traffic_bytes_per_launch")
 
 
+def resolve_query_order(requested: str, w, op: str):
+    """The visit order a run uses: "none", "interleaved" or "levels", or None
+    when an order is requested for queries that are not pixel centres.
+    "auto" is the measured best: the interleaved Z-order for pixel-centre
+    queries, except the 2D pruned forward, which runs slower with it."""
+    if requested == "auto":
+        best = w.queries == "pixel_centres" and not (op == "forward_pruned" and w.dims == 2)
+        return "interleaved" if best else "none"
+    if requested != "none" and w.queries != "pixel_centres":
+        return None
+    return requested
+
+
 def launch_times(step, n, stream, host_us_per_step):
     """Mean duration (s) of ``n`` back-to-back launches of ``step``.
 
@@ -395,14 +408,9 @@ def main(argv=None):
         base["grad_out"] = make_grad_out(w).to(dev)
     sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(copies - 1)]
 
-    order_kind = args.query_order
-    if order_kind == "auto":
-        # the measured best: the interleaved Z-order for pixel-centre queries,
-        # except the 2D pruned forward, which runs slower with it
-        best = w.queries == "pixel_centres" and not (pruned and w.dims == 2)
-        order_kind = "interleaved" if best else "none"
-    if order_kind != "none" and w.queries != "pixel_centres":
-        print(f"bench.py: --query-order {order_kind} needs pixel-centre queries; "
+    order_kind = resolve_query_order(args.query_order, w, args.op)
+    if order_kind is None:
+        print(f"bench.py: --query-order {args.query_order} needs pixel-centre queries; "
               f"{w.name} has {w.queries!r}", file=sys.stderr)
         return 2
     order, order_build_us = None, None
