@@ -302,6 +302,29 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
     const int G = 1 << p.log2G;
     float* gtile = gtile_all + wave * kTile;   // this wave's tiles' gradient rows
 
+    // Phase-B lane roles (CPL channel chunks x NG point groups) and this lane's
+    // VEC channels of its tile's output gradient (0 on idle lanes), loaded
+    // first so that the row's latency overlaps phase A
+    const int g = lane / CPL, c = lane % CPL;
+    const int t = g >> p.log2G;
+    const bool chunk_live = c < p.nchunk;
+    const uint32_t cc = static_cast<uint32_t>(min(c, p.nchunk - 1));
+    const uint32_t lane_off_v = cc * 16u;  // in value
+    const __amdgpu_buffer_rsrc_t rval = buffer_of(p.value, p.value_bytes);
+    const __amdgpu_buffer_rsrc_t rgv = buffer_of(bp.grad_value, bp.grad_value_bytes);
+    const __amdgpu_buffer_rsrc_t rgo = buffer_of(bp.grad_out, bp.grad_out_bytes);
+    const int D = p.nchunk * VEC;
+    float gch[VEC];
+    {
+        const bool tile_live = wave_live && q0 + static_cast<uint32_t>(t) < static_cast<uint32_t>(p.nq);
+        const uint32_t row =
+            (image_q0 + query_at(p, q0 + static_cast<uint32_t>(t))) * static_cast<uint32_t>(p.M) + m;
+        const uint32_t goff = tile_live && chunk_live
+                                  ? row * bp.gout_head_bytes + cc * (VEC * sizeof(TG))
+                                  : kOutOfRange;
+        load_grad<TG, VEC>(rgo, goff, gch);
+    }
+
     // ---- Phase A: lane k fills slot k = i*NG + g.
     BwdSlot<NC, DIM> mine;           // this lane's sample (kept for phase D)
     int my_level = 0, my_x0 = 0, my_y0 = 0, my_z0 = 0, my_tile = 0;
@@ -330,32 +353,11 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
     }
     __syncthreads();
 
-    // ---- Phase B
-    const int g = lane / CPL, c = lane % CPL;
-    const int t = g >> p.log2G;
-    const bool chunk_live = c < p.nchunk;
-    const uint32_t cc = static_cast<uint32_t>(min(c, p.nchunk - 1));
-    const uint32_t lane_off_v = cc * 16u;  // in value
-    const __amdgpu_buffer_rsrc_t rval = buffer_of(p.value, p.value_bytes);
-    const __amdgpu_buffer_rsrc_t rgv = buffer_of(bp.grad_value, bp.grad_value_bytes);
-    const __amdgpu_buffer_rsrc_t rgo = buffer_of(bp.grad_out, bp.grad_out_bytes);
-
-    // this lane's VEC channels of the tile's output gradient (0 on idle lanes);
-    // the first group of each tile also keeps the row in LDS for phase C
-    const int D = p.nchunk * VEC;
-    float gch[VEC];
-    {
-        const bool tile_live = wave_live && q0 + static_cast<uint32_t>(t) < static_cast<uint32_t>(p.nq);
-        const uint32_t row =
-            (image_q0 + query_at(p, q0 + static_cast<uint32_t>(t))) * static_cast<uint32_t>(p.M) + m;
-        const uint32_t goff = tile_live && chunk_live
-                                  ? row * bp.gout_head_bytes + cc * (VEC * sizeof(TG))
-                                  : kOutOfRange;
-        load_grad<TG, VEC>(rgo, goff, gch);
-        if ((g & (G - 1)) == 0 && chunk_live) {
+    // ---- Phase B.  The first group of each tile keeps the tile's gradient
+    // row in LDS for phases C and D.
+    if ((g & (G - 1)) == 0 && chunk_live) {
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) gtile[t * D + c * VEC + e] = gch[e];
-        }
+        for (int e = 0; e < VEC; ++e) gtile[t * D + c * VEC + e] = gch[e];
     }
 
     const BwdSlot<NC, DIM>* my = &slots[wave][g];
