@@ -62,9 +62,14 @@ COUNTERS_FILES = {
     "linear": os.path.join(ROOT, "profiles", "msda_linear_counters.json"),
 }
 KERNEL_SOURCES = {
-    "forward": [os.path.join(CSRC, "msda_device.hpp"), os.path.join(CSRC, "msda_api.hip")],
-    "forward_fused": [os.path.join(CSRC, "msda_device.hpp"), os.path.join(CSRC, "msda_api.hip")],
-    "forward_pruned": [os.path.join(CSRC, "msda_device.hpp"), os.path.join(CSRC, "msda_api.hip")],
+    "forward": [os.path.join(CSRC, "msda_device.hpp"), os.path.join(CSRC, "msda_forward_impl.hpp"),
+                os.path.join(CSRC, "msda_api.hip")],
+    "forward_fused": [os.path.join(CSRC, "msda_device.hpp"),
+                      os.path.join(CSRC, "msda_forward_impl.hpp"),
+                      os.path.join(CSRC, "msda_api_fused.hip")],
+    "forward_pruned": [os.path.join(CSRC, "msda_device.hpp"),
+                       os.path.join(CSRC, "msda_forward_impl.hpp"),
+                       os.path.join(CSRC, "msda_api_pruned.hip")],
     "backward": [os.path.join(CSRC, "msda_device.hpp"), os.path.join(CSRC, "msda_backward.hpp"),
                  os.path.join(CSRC, "msda_backward_api.hip")],
     "linear": [os.path.join(CSRC, "msda_device.hpp"), os.path.join(CSRC, "msda_linear.hip")],
@@ -181,6 +186,79 @@ def launch_times(step, n, stream, host_us_per_step):
     b.record(stream)
     torch.cuda.synchronize()
     return a.elapsed_time(b) / 1e3 / n
+
+
+# Windows of the random-row calibration: L1-, L2- and Infinity-Cache-resident
+# and HBM-scale (powers of two).
+CALIB_WINDOWS = {"l1": 16 << 10, "l2": 2 << 20, "mall": 32 << 20, "hbm": 1 << 30}
+CALIB_LDS_MODES = {"lds_rows": 0, "lds_row_pairs": 1, "lds_broadcast": 2,
+                   "lds_half_rows_same_banks": 3, "lds_half_rows_other_banks": 4,
+                   "lds_corner_quads_swizzled": 5, "lds_corner_quads": 6,
+                   "lds_corner_quads_odd_pitch": 7, "lds_slot_words": 8}
+CLOCK_GHZ = 2.4
+NUM_CUS = 256
+
+
+def gather_ceilings(dev, windows=CALIB_WINDOWS, lds_modes=CALIB_LDS_MODES, stream_bytes=1 << 30,
+                    reps=5):
+    """Measured delivery rates of the hot path's access pattern (128-byte rows
+    at random positions, 8 lanes x 16 bytes each) from each memory level, and
+    of a coalesced HBM read stream: GB/s and bytes per CU-clock (at the 2.4 GHz
+    peak clock), the median of ``reps`` timed launches after one warm-up."""
+    import torch
+
+    from scale_deformable_attention_02_amd.binding import (calib_gather_global,
+                                                           calib_gather_lds, calib_stream)
+
+    blocks = NUM_CUS * 8
+    big = max(max(windows.values()), stream_bytes)
+    buf = torch.randint(0, 255, (big,), dtype=torch.uint8, device=dev)
+    sink = torch.empty(blocks * 256 * 16, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(launch):
+        launch()
+        times = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            nbytes = launch()
+            b.record(stream)
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b) / 1e3)
+        t = statistics.median(times)
+        return {"gbps": nbytes / t / 1e9,
+                "bytes_per_cu_clk": nbytes / t / (NUM_CUS * CLOCK_GHZ * 1e9)}
+
+    out = {}
+    for name, wb in windows.items():
+        iters = 1024 if name in ("mall", "hbm") else 4096
+        out[name] = timed(lambda: calib_gather_global(buf, wb, blocks, iters, sink))
+        out[name]["window_bytes"] = wb
+        if name in ("l1", "l2"):   # the same rows read half a row per 4 lanes
+            out[name + "_half_rows"] = timed(
+                lambda: calib_gather_global(buf, wb, blocks, iters, sink, lanes_per_row=4))
+    for name, mode in lds_modes.items():
+        out[name] = timed(lambda: calib_gather_lds(buf, mode, blocks, 4096, sink))
+    out["hbm_stream"] = timed(lambda: calib_stream(buf, stream_bytes, blocks, sink))
+    del buf, sink
+    return out
+
+
+def bench_calib(args):
+    """--op calib: the gather ceilings alone, as one JSON line."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    ceil = gather_ceilings(dev)
+    print(json.dumps({
+        "metric": "gather ceilings: random 128-byte rows per memory level (1 MI355X)",
+        "value": ceil["l1"]["gbps"], "unit": "GB/s (L1-resident random rows)",
+        "n_gpus": 1, "higher_is_better": True, "vs_baseline": None, "dtype": "u8",
+        "data": "synthetic", "config": {"workload": "gather calibration",
+                                        "clock_ghz_assumed": CLOCK_GHZ, "cus": NUM_CUS},
+        "ceilings": ceil}), flush=True)
+    return 0
 
 
 def cpu_baseline(w, inp, max_points=60_000_000, grad_out=None, threshold=None,
@@ -346,7 +424,7 @@ def main(argv=None):
     ap.add_argument("--config", default="detr_encoder",
                     help="workload name (default: the DETR encoder configuration)")
     ap.add_argument("--op", choices=("forward", "forward_fused", "forward_pruned", "backward",
-                                     "linear"),
+                                     "linear", "calib"),
                     default="forward",
                     help="time the forward (default), the forward with the fused front "
                          "end, the pruned forward, the backward entry point, or the value "
@@ -365,6 +443,8 @@ def main(argv=None):
                          "pruned forward), else none")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip timing the oracle (for profiler runs)")
+    ap.add_argument("--no-calibration", action="store_true",
+                    help="skip the gather-ceiling calibration (roofline.gather)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB "
                          "(a known-size reference for HBM byte counters)")
@@ -380,6 +460,8 @@ def main(argv=None):
 
     if args.op == "linear":
         return bench_linear(args)
+    if args.op == "calib":
+        return bench_calib(args)
 
     from scale_deformable_attention_02_amd import (msda3d_backward, msda3d_forward,
                                                    msda3d_forward_fused, msda3d_forward_pruned,
@@ -578,6 +660,24 @@ def main(argv=None):
             "traffic": traffic,
         },
     }
+    if not args.no_calibration:
+        # the gathered bytes per second against the measured delivery rate of
+        # the same access pattern: random 128-byte rows from an L1-resident
+        # window (the path corner rows take through the texture units), and
+        # the other ceilings beside it
+        ceil = gather_ceilings(dev, windows={"l1": CALIB_WINDOWS["l1"],
+                                             "l2": CALIB_WINDOWS["l2"]},
+                               lds_modes={"lds_rows": 0})
+        gathered = G / kernel_s / 1e9
+        result["roofline"]["gather"] = {
+            "gathered_gbps": gathered,
+            "ceiling": ceil["l1"]["gbps"],
+            "frac": gathered / ceil["l1"]["gbps"],
+            "ceiling_kind": "L1-resident random 128-byte rows (8 lanes x 16 B)",
+            "l2_ceiling": ceil["l2"]["gbps"],
+            "lds_ceiling": ceil["lds_rows"]["gbps"],
+            "hbm_stream": ceil["hbm_stream"]["gbps"],
+        }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(
             w, inp, grad_out=make_grad_out(w) if backward else None,

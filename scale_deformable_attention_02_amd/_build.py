@@ -10,11 +10,14 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libmsda.so")
-SOURCES = [os.path.join(CSRC, "msda_api.hip"), os.path.join(CSRC, "msda_backward_api.hip"),
-           os.path.join(CSRC, "msda_linear.hip"), os.path.join(CSRC, "msda_order.hip")]
+SOURCES = [os.path.join(CSRC, "msda_api.hip"), os.path.join(CSRC, "msda_api_fused.hip"),
+           os.path.join(CSRC, "msda_api_pruned.hip"), os.path.join(CSRC, "msda_backward_api.hip"),
+           os.path.join(CSRC, "msda_linear.hip"), os.path.join(CSRC, "msda_order.hip"),
+           os.path.join(CSRC, "msda_calib.hip")]
 DEPENDS = SOURCES + [os.path.join(CSRC, "msda_device.hpp"), os.path.join(CSRC, "msda_backward.hpp"),
+                     os.path.join(CSRC, "msda_forward_impl.hpp"),
                      os.path.join(CSRC, "msda_host.hpp"),
-                     os.path.join(INCLUDE, "msda.h")]
+                     os.path.join(INCLUDE, "msda.h"), os.path.join(INCLUDE, "msda_calib.h")]
 
 ARCH = "gfx950"
 

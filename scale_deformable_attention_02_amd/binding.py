@@ -35,10 +35,11 @@ STATUS = {
     7: "MSDA_ERR_LAUNCH",
 }
 
-# Every symbol include/msda.h declares.
+# Every symbol include/msda.h and include/msda_calib.h declare.
 EXPORTED = ("msda_forward", "msda3d_forward", "msda_forward_pruned", "msda3d_forward_pruned",
             "msda_forward_fused", "msda3d_forward_fused", "msda_backward", "msda3d_backward",
-            "msda_linear", "msda_query_order", "msda_status_string")
+            "msda_linear", "msda_query_order", "msda_status_string",
+            "msda_calib_gather_global", "msda_calib_gather_lds", "msda_calib_stream")
 
 _lib = None
 
@@ -93,6 +94,14 @@ def load_library() -> ctypes.CDLL:
     lib.msda_query_order.argtypes = [vp, i64, i64, ctypes.c_int, vp, i64, vp]
     lib.msda_status_string.restype = ctypes.c_char_p
     lib.msda_status_string.argtypes = [ctypes.c_int]
+    u64 = ctypes.c_uint64
+    ci = ctypes.c_int
+    lib.msda_calib_gather_global.restype = ci
+    lib.msda_calib_gather_global.argtypes = [vp, u64, ci, ci, ci, vp, vp]
+    lib.msda_calib_gather_lds.restype = ci
+    lib.msda_calib_gather_lds.argtypes = [vp, ci, ci, ci, vp, vp]
+    lib.msda_calib_stream.restype = ci
+    lib.msda_calib_stream.argtypes = [vp, u64, ci, vp, vp]
     _lib = lib
     return lib
 
@@ -456,3 +465,55 @@ def msda_query_order(spatial_shapes, level_major: bool = True, device=None, out=
     if status != 0:
         raise MsdaError(status, status_string(status))
     return out
+
+
+# ---------------------------------------------------------------------------
+# Gather-ceiling calibration (include/msda_calib.h): measurement kernels, not
+# part of the operator.  Each call enqueues one launch on torch's current
+# stream and returns the bytes it moves; the caller times it.
+# ---------------------------------------------------------------------------
+CALIB_THREADS = 256
+
+
+def _calib_check(status: int, name: str):
+    if status != 0:
+        raise MsdaError(status, f"{name}: {status_string(status)}")
+
+
+def calib_gather_global(buf: torch.Tensor, window_bytes: int, blocks: int, iters: int,
+                        sink: torch.Tensor, lanes_per_row: int = 8) -> int:
+    """Random 128-byte rows from the first ``window_bytes`` of ``buf``, read
+    by 8 lanes with one load each or by 4 lanes with two loads each."""
+    lib = load_library()
+    assert buf.is_cuda and sink.is_cuda and buf.numel() * buf.element_size() >= window_bytes
+    assert sink.numel() * sink.element_size() >= blocks * CALIB_THREADS * 16
+    st = lib.msda_calib_gather_global(buf.data_ptr(), window_bytes, lanes_per_row, blocks, iters,
+                                      sink.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    _calib_check(st, "msda_calib_gather_global")
+    return blocks * CALIB_THREADS * iters * 16
+
+
+def calib_gather_lds(fill: torch.Tensor, mode: int, blocks: int, iters: int,
+                     sink: torch.Tensor) -> int:
+    """16-byte reads per lane from a 64 KB LDS array in the pattern ``mode``
+    (0 random rows, 1 x-adjacent row pairs, 2 broadcast, 3 and 4 half rows on
+    the same or opposite banks, 5 and 6 the corner rows of bilinear samples
+    with and without swapped halves; include/msda_calib.h)."""
+    lib = load_library()
+    assert fill.is_cuda and sink.is_cuda and fill.numel() * fill.element_size() >= 65664
+    assert sink.numel() * sink.element_size() >= blocks * CALIB_THREADS * 16
+    st = lib.msda_calib_gather_lds(fill.data_ptr(), mode, blocks, iters, sink.data_ptr(),
+                                   torch.cuda.current_stream().cuda_stream)
+    _calib_check(st, "msda_calib_gather_lds")
+    return blocks * CALIB_THREADS * iters * 16
+
+
+def calib_stream(buf: torch.Tensor, nbytes: int, blocks: int, sink: torch.Tensor) -> int:
+    """A coalesced read of ``nbytes`` of ``buf``."""
+    lib = load_library()
+    assert buf.is_cuda and sink.is_cuda and buf.numel() * buf.element_size() >= nbytes
+    assert sink.numel() * sink.element_size() >= blocks * CALIB_THREADS * 16
+    st = lib.msda_calib_stream(buf.data_ptr(), nbytes, blocks, sink.data_ptr(),
+                               torch.cuda.current_stream().cuda_stream)
+    _calib_check(st, "msda_calib_stream")
+    return nbytes

@@ -44,6 +44,13 @@ STAGED = [
     # a level one pixel wide (the backward's x < W/2 window is empty) and an
     # odd width
     (2, "f32", 1, ((97, 1), (13, 3)), 16500, 4, 16, 4, "random_refs"),
+    # head rows that are not a power of two of 16-byte chunks in the large
+    # launches: 3 chunks of 4 lanes (fp32 D = 12, bf16 D = 24) and 12 chunks
+    # of 16 lanes (fp32 D = 48), with the pixel-centre and random layouts
+    (2, "f32", 2, ((60, 90), (30, 45), (15, 23), (8, 12)), 7191, 8, 12, 4, "pixel_centres"),
+    (2, "f32", 2, ((60, 90), (30, 45), (15, 23), (8, 12)), 7191, 8, 48, 4, "pixel_centres"),
+    (2, "bf16", 2, ((60, 90), (30, 45), (15, 23), (8, 12)), 7191, 8, 24, 4, "pixel_centres"),
+    (2, "f32", 1, ((60, 90), (30, 45), (15, 23), (8, 12)), 9000, 8, 12, 4, "random_refs"),
     # L * P = 9, P = 3: four tiles and two point groups per wave, G does not
     # divide P, so the forward takes the direct kernel with several tiles per
     # wave

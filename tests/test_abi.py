@@ -12,7 +12,12 @@ from scale_deformable_attention_02_amd import _build, binding
 from scale_deformable_attention_02_amd.binding import raw_call
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "msda.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
+
+
+def _header_text():
+    return "".join(open(h).read() for h in HEADERS)
 
 OK, NULL, DIM, DTYPE, UNSUP, ALIGN, OVERFLOW = 0, 1, 2, 3, 4, 5, 6
 A = 1 << 12   # a fake, suitably aligned non-null address (never dereferenced)
@@ -26,7 +31,7 @@ def lib():
 
 
 def _declared_functions():
-    text = open(HEADER).read()
+    text = _header_text()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(msda\w*)\s*\(", text)))
 
@@ -47,7 +52,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_argtypes_match_the_header(lib):
     # every bound entry point passes as many arguments as the header declares
-    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    text = re.sub(r"/\*.*?\*/", "", _header_text(), flags=re.S)
     for name in binding.EXPORTED:
         m = re.search(r"\b" + name + r"\s*\(([^)]*)\)", text)
         assert m, name
