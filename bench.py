@@ -15,8 +15,10 @@ inputs are reported beside it).
 Queries are visited in a Z-order (Morton) order of the pixels when the
 workload's queries are the pyramid's pixel centres, except in the 2D pruned
 forward (``--query-order``; the order depends only on the level shapes, so it
-is built once, before the timed steps, like any per-shape plan); every output
-is the same as in the raw query order, which ``--query-order none`` times.
+is built once, before the timed steps, like any per-shape plan: ``value`` and
+the kernel time exclude its build, whose own GPU time is reported as
+``query_order_build_us``); every output is the same as in the raw query order,
+which ``--query-order none`` times.
 Steps cycle over several distinct copies of the inputs whose total exceeds
 twice the 256 MB Infinity Cache, so each step reads its inputs from HBM
 rather than from a cache warmed by the previous step.
@@ -25,9 +27,12 @@ Prints one JSON line: sampled points/s over the timed steps (wall clock,
 synchronised on both sides), achieved effective HBM GB/s of the kernel against
 the 8 TB/s peak (roofline; the kernel time is the mean of the same number of
 launches run back to back behind a GPU spin and bracketed by one pair of HIP
-events on the launch stream), the oracle's CPU throughput on the same inputs
-(cpu_baseline), and the counter traffic recorded for this kernel under
-profiles/ when it is still current.
+events on the launch stream), the gathered bytes/s against the measured
+ceiling of the same access pattern (roofline.gather, from the calibration
+kernels of include/msda_calib.h), the oracle's CPU throughput on the same
+inputs over the host's threads and on one core (cpu_baseline), and the
+counter traffic recorded for this kernel under profiles/ when it is still
+current.
 """
 from __future__ import annotations
 
@@ -261,13 +266,40 @@ def bench_calib(args):
     return 0
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), or the platform's guess."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def host_threads() -> int:
+    """Threads for the all-cores oracle leg: the CPUs this process may run on,
+    capped by OMP_NUM_THREADS when it is set (the GPU machine's CPU share)."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    cap = os.environ.get("OMP_NUM_THREADS")
+    if cap and cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
+
+
 def cpu_baseline(w, inp, max_points=60_000_000, grad_out=None, threshold=None,
-                 min_seconds=10.0, max_passes=200):
-    """Time the oracle (single-threaded C) on the same inputs, bounded: at most
-    ``max_points`` sampled points per pass, passes repeated until
-    ``min_seconds`` have elapsed (or ``max_passes``).  The backward oracle when
-    ``grad_out`` is given, the fused-front-end oracle when ``inp`` holds
-    reference points, offsets and logits."""
+                 min_seconds=10.0, max_passes=200, threads=None):
+    """Time the oracle (plain C, one sample point at a time) on the same
+    inputs, bounded: at most ``max_points`` sampled points per pass, passes
+    repeated until ``min_seconds`` have elapsed (or ``max_passes``).  Two legs:
+    the single-threaded oracle on the whole sample, and the same function over
+    ``threads`` host threads, each on its own disjoint (image, query range)
+    slices of the sample.  The backward oracle when ``grad_out`` is given, the
+    fused-front-end oracle when ``inp`` holds reference points, offsets and
+    logits."""
+    import concurrent.futures
+
     import numpy as np
 
     import oracle
@@ -294,35 +326,57 @@ def cpu_baseline(w, inp, max_points=60_000_000, grad_out=None, threshold=None,
     shapes = inp["spatial_shapes"].numpy()
     starts = inp["level_start_index"].numpy()
     if fused:
-        args = (value, shapes, starts,
-                np.ascontiguousarray(inp["reference_points"][:nb, :nq].numpy()),
-                np.ascontiguousarray(inp["sampling_offsets"][:nb, :nq].numpy()),
-                inp["attention_logits"][:nb, :nq].double().numpy())
+        per_q = (np.ascontiguousarray(inp["reference_points"][:nb, :nq].numpy()),
+                 np.ascontiguousarray(inp["sampling_offsets"][:nb, :nq].numpy()),
+                 inp["attention_logits"][:nb, :nq].double().numpy())
     else:
-        loc = np.ascontiguousarray(inp["sampling_locations"][:nb, :nq].numpy())
-        attw = inp["attention_weights"][:nb, :nq].double().numpy()
-        args = (value, shapes, starts, loc, attw)
+        per_q = (np.ascontiguousarray(inp["sampling_locations"][:nb, :nq].numpy()),
+                 inp["attention_weights"][:nb, :nq].double().numpy())
     if grad_out is not None:
-        args += (grad_out[:nb, :nq].double().numpy(),)
-    if threshold is not None:
-        args += (threshold,)
-    passes = 0
-    t0 = time.perf_counter()
-    while True:
-        fn(*args)
-        passes += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_seconds or passes >= max_passes:
-            break
+        per_q += (grad_out[:nb, :nq].double().numpy(),)
+    tail = (threshold,) if threshold is not None else ()
+
+    def call(n0, n1, q0, q1):
+        # the same entry point on images n0..n1-1, queries q0..q1-1 (the
+        # value pyramid of those images is shared, read-only)
+        fn(value[n0:n1], shapes, starts,
+           *(np.ascontiguousarray(a[n0:n1, q0:q1]) for a in per_q), *tail)
+
+    def timed(run):
+        passes = 0
+        t0 = time.perf_counter()
+        while True:
+            run()
+            passes += 1
+            dt = time.perf_counter() - t0
+            if dt >= min_seconds or passes >= max_passes:
+                return passes, dt
+
+    model = cpu_model()
+    passes, dt = timed(lambda: call(0, nb, 0, nq))
     points = nb * nq * per_query * passes
-    return {
-        "value": points / dt,
-        "unit": "sampled points/s",
-        "cores": 1,
-        "kind": "oracle",
+    single = {
+        "value": points / dt, "unit": "sampled points/s", "cores": 1, "kind": "oracle",
         "sample": f"{sample}, {passes} passes: {points} sampled points in {dt:.2f} s, "
-                  f"single-threaded C oracle (fp64 accumulate) on "
-                  f"{platform.processor() or platform.machine()}",
+                  f"single-threaded C oracle (fp64 accumulate) on {model}",
+    }
+    T = threads or host_threads()
+    # disjoint slices: every image cut into query ranges, about 4 per thread
+    pieces = max(1, (4 * T + nb - 1) // nb)
+    step = max(1, -(-nq // pieces))
+    jobs = [(n, n + 1, q0, min(nq, q0 + step)) for n in range(nb) for q0 in range(0, nq, step)]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=T) as pool:
+        def run_all():
+            list(pool.map(lambda j: call(*j), jobs))
+        passes_t, dt_t = timed(run_all)
+    points_t = nb * nq * per_query * passes_t
+    return {
+        "value": points_t / dt_t, "unit": "sampled points/s", "cores": T, "kind": "oracle",
+        "sample": f"{sample}, {passes_t} passes: {points_t} sampled points in {dt_t:.2f} s, "
+                  f"the C oracle over {T} host threads, {len(jobs)} disjoint (image, query "
+                  f"range) slices per pass, on {model}",
+        "cpu_model": model,
+        "single_core": single,
     }
 
 

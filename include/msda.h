@@ -74,9 +74,12 @@ typedef enum {
     MSDA_ERR_ALIGN = 5,       /* value/out not 16-byte aligned, locations,
                                  weights not 4-byte aligned, shapes/starts
                                  not 8-byte aligned                        */
-    MSDA_ERR_OVERFLOW = 6,    /* one image's value (S*M*D elements) is
-                                 2^31 bytes or more (with a query order:
-                                 also its locations)                       */
+    MSDA_ERR_OVERFLOW = 6,    /* 2^31 bytes or more in one image's value
+                                 (S*M*D elements), or in one query's
+                                 locations (M*L*P*2 or *3 floats; in the
+                                 backward also its output gradient), or,
+                                 with a query order, in one image's
+                                 locations                                 */
     MSDA_ERR_LAUNCH = 7       /* the HIP launch failed                     */
 } msda_status;
 

@@ -30,15 +30,24 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "msda_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# MSDA_ORACLE_SANITIZE=1 selects a build of the same source with
+# AddressSanitizer and UndefinedBehaviorSanitizer (every finding aborts); the
+# process must then preload the ASan runtime, e.g.
+#   LD_PRELOAD=$(gcc -print-file-name=libasan.so) ASAN_OPTIONS=detect_leaks=0 \
+#   MSDA_ORACLE_SANITIZE=1 python -m pytest tests -m "not gpu"
+SANITIZE = os.environ.get("MSDA_ORACLE_SANITIZE", "0") not in ("", "0")
+_LIB_PATH = os.path.join(_HERE, "liboracle_san.so" if SANITIZE else "liboracle.so")
+_SAN_FLAGS = ["-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+              "-fno-sanitize-recover=all"]
 _lib = None
 
 
 def build() -> str:
-    """Compile the oracle into ``oracle/liboracle.so`` (always rebuilds)."""
+    """Compile the oracle into ``oracle/liboracle.so`` (always rebuilds; with
+    MSDA_ORACLE_SANITIZE=1 the sanitizer build ``oracle/liboracle_san.so``)."""
     tmp = _LIB_PATH + ".tmp"
     cmd = ["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math",
-           "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"]
+           "-fPIC", "-shared", *(_SAN_FLAGS if SANITIZE else []), "-o", tmp, _SRC, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, _LIB_PATH)
     return _LIB_PATH

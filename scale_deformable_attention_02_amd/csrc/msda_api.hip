@@ -42,8 +42,9 @@ const char* msda_status_string(int status) {
             return "misaligned pointer (value/out need 16 bytes, locations/weights 4, "
                    "shapes/starts 8)";
         case MSDA_ERR_OVERFLOW:
-            return "one image's value tensor is 2^31 bytes or larger (or S, M, Lq >= 2^31; "
-                   "with a query order, also one image's locations or output gradient)";
+            return "one image's value tensor, or one query's locations or output gradient, "
+                   "is 2^31 bytes or larger (or S, M, Lq >= 2^31; with a query order, also "
+                   "one image's locations or output gradient)";
         case MSDA_ERR_LAUNCH: return "HIP kernel launch failed";
         default: return "unknown status";
     }

@@ -109,11 +109,16 @@ int backward(const void* value, int value_dtype, const int64_t* spatial_shapes,
     const int64_t image_bytes = S * M * head_bytes;
     const int64_t value_limit = elem == 2 ? kLimit / 2 : kLimit;
     if (gimage_bytes >= kLimit || image_bytes >= value_limit) return MSDA_ERR_OVERFLOW;
-
-    if (query_order && Lq > 0) {
+    // one query's locations and output gradient must stay below 2^31 bytes
+    // (a launch covers at least one query); with this, Lq times either
+    // stays far inside int64
+    {
         const int64_t loc_q = M * L * P * DIM * 4, gout_q = M * gout_head_bytes;
         const int64_t per_q = loc_q > gout_q ? loc_q : gout_q;
-        if (Lq * per_q >= kLimit || Lq * M >= (int64_t{1} << 30)) return MSDA_ERR_OVERFLOW;
+        if (per_q >= kLimit) return MSDA_ERR_OVERFLOW;
+        if (query_order && Lq > 0 &&
+            (Lq * per_q >= kLimit || Lq * M >= (int64_t{1} << 30)))
+            return MSDA_ERR_OVERFLOW;
     }
 
     const hipStream_t hs = static_cast<hipStream_t>(stream);

@@ -159,6 +159,9 @@ int forward(const void* value, int value_dtype, const int64_t* spatial_shapes,
     const int64_t loc_per_query = M * LP * DIM * 4;
     const int64_t attw_per_query = M * LP * 4;
     const int64_t kTileLimit = int64_t{1} << 30;
+    // one query's locations must stay below 2^31 bytes (a launch covers at
+    // least one query); with this, Lq * loc_per_query stays far inside int64
+    if (loc_per_query >= kLimit) return MSDA_ERR_OVERFLOW;
     const bool whole_images = Lq * loc_per_query < kLimit && Lq * M < kTileLimit;
     if (query_order && !whole_images) return MSDA_ERR_OVERFLOW;
     int64_t nb = 0, nq = Lq;

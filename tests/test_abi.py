@@ -129,6 +129,9 @@ def test_overflow(lib):
     assert call(S=1 << 31, M=1, D=4) == OVERFLOW
     assert call(Lq=1 << 31) == OVERFLOW
     assert call(M=1 << 31, D=4) == OVERFLOW
+    # one query's locations take 2^31 bytes (M = 2^22 heads of L*P = 64
+    # points): rejected on the host, whatever the value's size
+    assert call(S=1, M=1 << 22, D=4, L=4, P=16) == OVERFLOW
 
 
 def test_binding_rejects_cpu_tensors(lib):
@@ -178,6 +181,8 @@ def test_backward_unsupported_misaligned_overflow(lib):
     # fp32 gradient image S*M*D*4 must stay below 2^31 bytes, also for bf16 value
     assert bcall(S=(1 << 31) // (8 * 32 * 4), M=8, D=32, dtype=1) == OVERFLOW
     assert bcall(M=1 << 31, D=4) == OVERFLOW
+    # one query's locations take 2^31 bytes: rejected before the gradient fill
+    assert bcall(S=1, M=1 << 22, D=4, L=4, P=16) == OVERFLOW
 
 
 # ---- fused front end: the forward's checks plus the reference-point pointer
