@@ -667,10 +667,13 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
         // are summed across lanes, and lane (c4, es) then adds channel
         // 4*c4 + es of the total: one atomic per channel, the R lanes of a
         // group covering one contiguous row.
-        const int rl = 1 << log2R;               // lanes per row (4 <= R <= 64)
+        // lanes per row: R = D rounded up to a power of two = CPL * VEC
+        // (4 <= R <= 64), a constant here, so that the entry-subset sums
+        // below are lane moves inside the VALU
+        constexpr int rl = CPL * VEC;
+        constexpr int q4 = rl / 4;               // lanes per entry subset
         const int ngroups = kThreads / rl;
         const int grp = tid / rl, ch = tid % rl;
-        const int q4 = rl >> 2;                  // lanes per entry subset
         const int c4 = ch & (q4 - 1), es = ch / q4;
         const int chan = 4 * c4 + es;
         // lanes past D (D not a power of two) read the last chunk and never store
@@ -728,8 +731,8 @@ __global__ __launch_bounds__(WAVES * kWave) void msda_backward_kernel(BwdParams 
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     tot[u] = a0[u] + a1[u];
-                    tot[u] += __shfl_xor(tot[u], q4, kWave);
-                    tot[u] += __shfl_xor(tot[u], 2 * q4, kWave);
+                    tot[u] = xor_combine(tot[u], q4, AddOp());
+                    tot[u] = xor_combine(tot[u], 2 * q4, AddOp());
                 }
                 // channel 4*c4 + es of the total, picked by the bits of es
                 const float lo = (es & 1) ? tot[1] : tot[0];
