@@ -499,6 +499,8 @@ def main(argv=None):
                     help="skip timing the oracle (for profiler runs)")
     ap.add_argument("--no-calibration", action="store_true",
                     help="skip the gather-ceiling calibration (roofline.gather)")
+    ap.add_argument("--out-dtype", choices=("f32", "bf16"), default=None,
+                    help="output dtype of the forward ops (default: the workload's)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB "
                          "(a known-size reference for HBM byte counters)")
@@ -526,6 +528,8 @@ def main(argv=None):
                                                              make_grad_out, make_inputs)
 
     w = CONFIGS[args.config]
+    if args.out_dtype is not None and args.op != "backward":
+        w = w.with_(out_dtype=args.out_dtype)
     dev = torch.device("cuda:0")
     backward = args.op == "backward"
     fused = args.op == "forward_fused"
@@ -667,7 +671,9 @@ def main(argv=None):
     order_label = ("none" if order is None else
                    "z-order, levels interleaved" if order_kind == "interleaved"
                    else "z-order, level by level")
-    traffic = counters_for(w.name, args.op, order_label)
+    # committed counters were taken with the workload's own output dtype
+    traffic = (counters_for(w.name, args.op, order_label)
+               if w.out_dtype == CONFIGS[w.name].out_dtype else None)
     result = {
         "metric": (METRIC_BACKWARD if backward else METRIC_FUSED if fused
                    else METRIC_PRUNED if pruned else METRIC),
