@@ -27,7 +27,8 @@ Prints one JSON line: sampled points/s over the timed steps (wall clock,
 synchronised on both sides), achieved effective HBM GB/s of the kernel against
 the 8 TB/s peak (roofline; the kernel time is the mean of the same number of
 launches run back to back behind a GPU spin and bracketed by one pair of HIP
-events on the launch stream), the gathered bytes/s against the measured
+events on the launch stream; ``kernel_us_single`` gives min, median, p90 and
+max of launches timed one at a time), the gathered bytes/s against the measured
 ceiling of the same access pattern (roofline.gather, from the calibration
 kernels of include/msda_calib.h), the oracle's CPU throughput on the same
 inputs over the host's threads and on one core (cpu_baseline), and the
@@ -160,6 +161,25 @@ def resolve_query_order(requested: str, w, op: str):
     if requested != "none" and w.queries != "pixel_centres":
         return None
     return requested
+
+
+def launch_distribution(step, n, stream):
+    """min / median / p90 / max (us) of ``n`` launches of ``step``, each timed
+    alone: an event pair around it, then a synchronize before the next, so a
+    figure includes one launch's dispatch latency and no neighbour's tail."""
+    import torch
+
+    ts = []
+    for i in range(n):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) * 1e3)
+    ts.sort()
+    return {"n": n, "min": ts[0], "median": ts[n // 2], "p90": ts[min(n - 1, (9 * n) // 10)],
+            "max": ts[-1]}
 
 
 def launch_times(step, n, stream, host_us_per_step):
@@ -641,6 +661,9 @@ def main(argv=None):
 
     # back-to-back on one input set: inputs stay in L2/Infinity Cache
     warm_s = launch_times(lambda i: step(0), 20, stream, host_s / args.steps * 1e6)
+    # the spread: launches timed one at a time (an event pair each, idle GPU
+    # between them), inputs cycled as in the timed steps
+    dist = launch_distribution(step, max(args.steps, 20), stream)
 
     unfused_us = None
     if fused or pruned:
@@ -700,6 +723,7 @@ def main(argv=None):
         "gathered_gbps": G / kernel_s / 1e9,
         "kernel_us_mean": kernel_s * 1e6,
         "kernel_us_warm": warm_s * 1e6,
+        "kernel_us_single": dist,
         "query_order_build_us": order_build_us,
         "bytes_per_launch": {"compulsory": U, "gathered": G},
         "unfused_pipeline_us_per_step": unfused_us if fused else None,
