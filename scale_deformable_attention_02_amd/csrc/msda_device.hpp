@@ -573,8 +573,19 @@ __device__ __forceinline__ Slot<NC> dead_slot(uint32_t invalid) {
 // Direct kernel: one pass of T tiles per wave, every corner gathered from HBM
 // (through L2/L1).  Used for small problems and as the general path.
 // ---------------------------------------------------------------------------
+// In 3D the kernel is bound by the texture path and its misses; asking for 8
+// waves per SIMD (at most 64 VGPRs; 54 for fp32 D=32, which with 17 KB of LDS
+// per block lets 9 waves per SIMD run) hides more of them than the 67 VGPRs
+// the compiler picks on its own (7 waves): 1502 against 1585 us on the
+// 64^3..8^3 volume.  Rows of 8 to 32 lanes only: at 64 lanes, and at 2 or 4
+// with bf16 output, 64 VGPRs would spill.
+template <int DIM, int CPL>
+constexpr int direct_waves_per_eu() { return DIM == 3 && CPL >= 8 && CPL <= 32 ? 8 : 1; }
+
 template <typename TV, typename TO, int DIM, int CPL, bool FUSED = false, bool PRUNE = false>
-__global__ __launch_bounds__(kBlockThreads) void msda_forward_kernel(Params p) {
+__global__ __launch_bounds__(kBlockThreads)
+__attribute__((amdgpu_waves_per_eu(direct_waves_per_eu<DIM, CPL>())))
+void msda_forward_kernel(Params p) {
     constexpr int NC = DIM == 2 ? 4 : 8;     // corners per sample
     constexpr int NG = kWave / CPL;          // point groups per wave
     constexpr int VEC = ValueTraits<TV>::kVec;
