@@ -1,4 +1,5 @@
-"""Oracle of the visit order for pixel-centre queries (test infrastructure only).
+"""Oracle of the visit orders (test infrastructure only): for pixel-centre
+queries, and for queries given by a point each.
 
 Only the tests, the smoke check and the benchmark's CPU-baseline leg may
 import this module; the HIP library never calls it and the two share no code.
@@ -15,6 +16,15 @@ and the pixels are sorted by (key, level, index in the level), or by (level,
 key, index) for the level-major order.  This module computes exactly that
 with integer arithmetic and one stable sort (the library instead counts each
 pixel's rank in closed form, without sorting).
+
+Queries whose reference points depend on the data (the decoder's learned
+reference points, "What is Deformable Attention", reference position) are
+ordered by one point each, in normalized coordinates: along every axis the
+point gets the cell floor(x * 2^B) of a grid of 2^B cells over the unit
+interval, clamped to [0, 2^B - 1] (a NaN coordinate counts as 0), with B = 16
+in 2D and 10 in 3D (a 32- or 30-bit key); the product x * 2^B is taken in
+fp32, where scaling by a power of two is exact.  The queries are sorted by
+(Morton key of the cells, query index).
 """
 from __future__ import annotations
 
@@ -45,15 +55,37 @@ def pixel_cells(shapes, dims: int):
     return np.concatenate(levels), np.concatenate(index), np.concatenate(cells)
 
 
-def morton_key(cells: np.ndarray) -> np.ndarray:
+def morton_key(cells: np.ndarray, bits: int = CELL_BITS) -> np.ndarray:
     """Z-order key of cell coordinates [S, dims]: bit b of axis d goes to key
     bit dims*b + d."""
     dims = cells.shape[1]
     key = np.zeros(cells.shape[0], dtype=np.int64)
-    for b in range(CELL_BITS):
+    for b in range(bits):
         for d in range(dims):
             key |= ((cells[:, d] >> b) & 1) << (dims * b + d)
     return key
+
+
+def point_bits(dims: int) -> int:
+    """Cells per axis (as a power of two) of the points order."""
+    return 16 if dims == 2 else 10
+
+
+def point_cells(points) -> np.ndarray:
+    """Cell coordinates [Lq, dims] of points [Lq, dims] (column 0 = x)."""
+    pts = np.asarray(points, dtype=np.float32)
+    bits = point_bits(pts.shape[1])
+    scaled = pts * np.float32(1 << bits)            # exact: a power of two
+    scaled = np.where(np.isnan(scaled), np.float32(0), scaled)
+    return np.clip(np.floor(scaled), 0, (1 << bits) - 1).astype(np.int64)
+
+
+def points_order_oracle(points) -> np.ndarray:
+    """The visit order (int64 [Lq]) of queries given by one point each: entry
+    r is the query of rank r by (Morton key of its cell, query index)."""
+    cells = point_cells(points)
+    key = morton_key(cells, point_bits(cells.shape[1]))
+    return np.lexsort((np.arange(len(key)), key)).astype(np.int64)
 
 
 def query_order_oracle(shapes, level_major: bool) -> np.ndarray:

@@ -97,3 +97,73 @@ def test_permutation_and_tie_rules(shapes):
     if dims == 2 and shapes[0] == (1, 1500):
         # a single-row level wider than the grid: raster order is preserved
         assert (major[:1500] == np.arange(1500)).all()
+
+
+# ---- the order of queries given by one point each (data-dependent reference
+# points): Morton key of the point's cell on a 2^16 (2D) or 2^10 (3D) grid,
+# ties by query index.
+
+from oracle.order import point_cells, points_order_oracle  # noqa: E402
+
+
+def test_points_quadrant_centres_follow_the_z_pattern():
+    # the four quadrant centres, given in a scrambled order: the Z pattern is
+    # (x low, y low), (x high, y low), (x low, y high), (x high, y high)
+    pts = np.array([[0.75, 0.75], [0.25, 0.75], [0.75, 0.25], [0.25, 0.25]], np.float32)
+    assert points_order_oracle(pts).tolist() == [3, 2, 1, 0]
+    # octant centres in 3D: x is the lowest key bit, then y, then z
+    oct_ = np.array([[x, y, z] for z in (0.75, 0.25) for y in (0.75, 0.25) for x in (0.75, 0.25)],
+                    np.float32)
+    order = points_order_oracle(oct_)
+    got = [tuple(oct_[i]) for i in order]
+    want = [(x, y, z) for z in (0.25, 0.75) for y in (0.25, 0.75) for x in (0.25, 0.75)]
+    assert got == want
+
+
+@pytest.mark.parametrize("dims,k", [(2, 1), (2, 3), (2, 5), (3, 1), (3, 3)])
+def test_points_order_of_pixel_centres_matches_the_pixel_order(dims, k):
+    # a single 2^k-per-axis level: the pixel centres (j + 1/2) / 2^k lie in
+    # cells j * 2^(B-k) + 2^(B-k-1), whose high bits are j, so both orders are
+    # the Morton order of the pixels (computed independently: the pixel order
+    # from its own 10-bit cells)
+    e = 1 << k
+    shape = (e,) * dims
+    idx = np.arange(e ** dims)
+    coords = []
+    rest = idx
+    for _ in range(dims):                  # x fastest
+        coords.append(rest % e)
+        rest = rest // e
+    pts = np.stack([(c + 0.5) / e for c in coords], axis=1).astype(np.float32)
+    assert points_order_oracle(pts).tolist() == query_order_oracle([shape], False).tolist()
+
+
+def test_points_cells_clamp_and_nan():
+    pts = np.array([[np.nan, 0.5], [-0.25, 1.0], [2.0, np.inf], [-np.inf, 0.999999]], np.float32)
+    c = point_cells(pts)
+    top = (1 << 16) - 1
+    assert c.tolist() == [[0, 32768], [0, top], [top, top], [0, int(np.floor(np.float32(0.999999) * 65536))]]
+
+
+def test_points_order_is_a_stable_sort_by_key():
+    rng = np.random.default_rng(7)
+    for dims in (2, 3):
+        # clustered points with exact duplicates: ties go by query index
+        pts = rng.random((500, dims)).astype(np.float32)
+        pts[100:140] = pts[3]
+        order = points_order_oracle(pts)
+        assert sorted(order.tolist()) == list(range(500))
+        cells = point_cells(pts)
+        bits = 16 if dims == 2 else 10
+        # key by explicit bit interleaving, written independently of morton_key
+        def key(c):
+            k = 0
+            for b in range(bits):
+                for d in range(dims):
+                    k |= ((int(c[d]) >> b) & 1) << (dims * b + d)
+            return k
+        keys = [key(cells[i]) for i in order]
+        assert all(a <= b for a, b in zip(keys, keys[1:]))
+        for a, b, ka, kb in zip(order, order[1:], keys, keys[1:]):
+            if ka == kb:
+                assert a < b
