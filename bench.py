@@ -151,14 +151,16 @@ def counters_for(workload_name: str, op: str = "forward", query_order: str = "no
 
 
 def resolve_query_order(requested: str, w, op: str):
-    """The visit order a run uses: "none", "interleaved" or "levels", or None
-    when an order is requested for queries that are not pixel centres.
+    """The visit order a run uses: "none", "interleaved" or "levels" (the
+    pixel-centre orders), "points" (the order of one point per query: the
+    first image's first sampling location of each query), or None when a
+    pixel-centre order is requested for queries that are not pixel centres.
     "auto" is the measured best: the interleaved Z-order for pixel-centre
     queries, except the 2D pruned forward, which runs slower with it."""
     if requested == "auto":
         best = w.queries == "pixel_centres" and not (op == "forward_pruned" and w.dims == 2)
         return "interleaved" if best else "none"
-    if requested != "none" and w.queries != "pixel_centres":
+    if requested in ("levels", "interleaved") and w.queries != "pixel_centres":
         return None
     return requested
 
@@ -509,12 +511,13 @@ def main(argv=None):
                     help="attention-weight threshold of --op forward_pruned "
                          "(default 0.8 / (L*P): about half the samples of softmaxed "
                          "N(0,1) logits)")
-    ap.add_argument("--query-order", choices=("auto", "none", "levels", "interleaved"),
+    ap.add_argument("--query-order", choices=("auto", "none", "levels", "interleaved", "points"),
                     default="auto",
                     help="visit order of the queries: a Z-order of the pixels with the "
-                         "levels interleaved or level by level, or none (the raw order); "
-                         "auto = interleaved for pixel-centre workloads (except the 2D "
-                         "pruned forward), else none")
+                         "levels interleaved or level by level, a Z-order of one point per "
+                         "query (the first image's first sampling locations), or none (the "
+                         "raw order); auto = interleaved for pixel-centre workloads (except "
+                         "the 2D pruned forward), else none")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip timing the oracle (for profiler runs)")
     ap.add_argument("--no-calibration", action="store_true",
@@ -543,7 +546,7 @@ def main(argv=None):
                                                    msda3d_forward_fused, msda3d_forward_pruned,
                                                    msda_backward, msda_forward,
                                                    msda_forward_fused, msda_forward_pruned,
-                                                   msda_query_order)
+                                                   msda_query_order, msda_query_order_points)
     from scale_deformable_attention_02_amd.workloads import (CONFIGS, make_fused_inputs,
                                                              make_grad_out, make_inputs)
 
@@ -574,7 +577,17 @@ def main(argv=None):
               f"{w.name} has {w.queries!r}", file=sys.stderr)
         return 2
     order, order_build_us = None, None
-    if order_kind != "none":
+    if order_kind == "points":
+        # one point per query: the first image's first sampling location, or
+        # its reference point for the fused front end (built
+        # before the timed steps, like a per-batch plan; its GPU time reported)
+        pts = (base["reference_points"][0] if fused
+               else base["sampling_locations"][0, :, 0, 0, 0, :]).contiguous()
+        order = msda_query_order_points(pts)
+        torch.cuda.synchronize()
+        order_build_us = launch_times(lambda i: msda_query_order_points(pts, out=order), 10,
+                                      torch.cuda.current_stream(dev), 200.0) * 1e6
+    elif order_kind != "none":
         # built once per pyramid shape, before the timed steps; its GPU time is
         # reported (mean of back-to-back rebuilds, host overhead excluded)
         order = msda_query_order(w.shapes, order_kind == "levels", device=dev)
@@ -693,6 +706,7 @@ def main(argv=None):
     achieved = U / kernel_s / 1e9
     order_label = ("none" if order is None else
                    "z-order, levels interleaved" if order_kind == "interleaved"
+                   else "z-order of one point per query" if order_kind == "points"
                    else "z-order, level by level")
     # committed counters were taken with the workload's own output dtype
     traffic = (counters_for(w.name, args.op, order_label)

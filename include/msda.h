@@ -294,6 +294,33 @@ int msda_query_order(const int64_t* spatial_shapes, int64_t L, int64_t dims,
                      void* stream);
 
 /*
+ * Query order for queries given by one point each, such as a decoder's
+ * reference points, which depend on the data ("What is Deformable
+ * Attention", reference position): queries whose points are close are
+ * visited together.  Fills query_order with a permutation of 0..Lq-1 for the
+ * query_order argument of the entry points above.  That argument is one
+ * permutation shared by the N images, so the caller picks the points it is
+ * built from (for instance those of the first image).
+ *   points       device float [Lq][dims], normalized (x, y) or (x, y, z),
+ *                4-byte aligned
+ *   Lq, dims     queries; 2 or 3
+ *   query_order  device int32 [Lq], overwritten
+ * Along every axis a point gets the cell floor(x * 2^B) of a grid of 2^B
+ * cells over [0, 1] (the product taken in fp32), clamped to [0, 2^B - 1], a
+ * NaN coordinate counting as 0; B = 16 in 2D and 10 in 3D.  Its key is the
+ * Z-order (Morton) code of the cell, bit b of the x cell at key bit dims*b,
+ * of y at dims*b+1, of z at dims*b+2.  The queries are sorted by (key, query
+ * index); query_order[r] is the query of rank r.  The kernel counts each
+ * query's rank by comparing keys (O(Lq^2) work, about 60 us at Lq = 22,223),
+ * so nothing is sorted and nothing is allocated.  Asynchronous on `stream`.
+ * Lq == 0 is a successful no-op.
+ * Errors: MSDA_ERR_DIM (dims not 2 or 3, Lq < 0); MSDA_ERR_NULL;
+ * MSDA_ERR_ALIGN; MSDA_ERR_OVERFLOW (Lq >= 2^30); MSDA_ERR_LAUNCH.
+ */
+int msda_query_order_points(const float* points, int64_t Lq, int64_t dims,
+                            int32_t* query_order, void* stream);
+
+/*
  * Dense projection on the matrix cores: y = x * weight^T + bias.
  *   x       [R][K]     x_dtype (MSDA_F32 or MSDA_BF16), 16-byte aligned
  *   weight  [N][K]     same dtype as x, 16-byte aligned

@@ -38,7 +38,7 @@ STATUS = {
 # Every symbol include/msda.h and include/msda_calib.h declare.
 EXPORTED = ("msda_forward", "msda3d_forward", "msda_forward_pruned", "msda3d_forward_pruned",
             "msda_forward_fused", "msda3d_forward_fused", "msda_backward", "msda3d_backward",
-            "msda_linear", "msda_query_order", "msda_status_string",
+            "msda_linear", "msda_query_order", "msda_query_order_points", "msda_status_string",
             "msda_calib_gather_global", "msda_calib_gather_lds", "msda_calib_stream")
 
 _lib = None
@@ -92,6 +92,8 @@ def load_library() -> ctypes.CDLL:
     lib.msda_linear.argtypes = [vp, ctypes.c_int, vp, vp, vp, ctypes.c_int, i64, i64, i64, vp]
     lib.msda_query_order.restype = ctypes.c_int
     lib.msda_query_order.argtypes = [vp, i64, i64, ctypes.c_int, vp, i64, vp]
+    lib.msda_query_order_points.restype = ctypes.c_int
+    lib.msda_query_order_points.argtypes = [vp, i64, i64, vp, vp]
     lib.msda_status_string.restype = ctypes.c_char_p
     lib.msda_status_string.argtypes = [ctypes.c_int]
     u64 = ctypes.c_uint64
@@ -462,6 +464,38 @@ def msda_query_order(spatial_shapes, level_major: bool = True, device=None, out=
     s = stream if stream is not None else torch.cuda.current_stream(out.device)
     status = raw_query_order_call(shapes.data_ptr(), L, dims, 1 if level_major else 0,
                                   out.data_ptr(), S, s.cuda_stream)
+    if status != 0:
+        raise MsdaError(status, status_string(status))
+    return out
+
+
+def raw_query_order_points_call(points_ptr: int, Lq: int, dims: int, order_ptr: int,
+                                stream: int = 0) -> int:
+    """Call msda_query_order_points with raw device pointers; returns the
+    msda_status."""
+    return load_library().msda_query_order_points(points_ptr, Lq, dims, order_ptr, stream)
+
+
+def msda_query_order_points(points, out=None, stream=None) -> torch.Tensor:
+    """Visit order for queries given by one point each (data-dependent
+    reference points): int32 [Lq], the queries ranked by (Z-order key of the
+    point's cell on a 2^16 (2D) or 2^10 (3D) grid per axis, query index).
+    ``points`` is a float32 GPU tensor [Lq, 2] = (x, y) or [Lq, 3] =
+    (x, y, z) in normalized coordinates.  The order is one permutation for all
+    images of a call, so pass the points of the image it should follow."""
+    if (not isinstance(points, torch.Tensor) or not points.is_cuda or points.dim() != 2
+            or points.shape[1] not in (2, 3) or points.dtype != torch.float32):
+        raise ValueError("points must be a float32 GPU tensor [Lq, 2] or [Lq, 3]")
+    points = points.contiguous()
+    Lq, dims = points.shape
+    if out is None:
+        out = torch.empty((Lq,), dtype=torch.int32, device=points.device)
+    elif (not out.is_cuda or out.dtype != torch.int32 or tuple(out.shape) != (Lq,)
+          or not out.is_contiguous() or out.device != points.device):
+        raise ValueError(f"out must be a contiguous int32 [{Lq}] tensor on the points' device")
+    s = stream if stream is not None else torch.cuda.current_stream(points.device)
+    status = raw_query_order_points_call(points.data_ptr(), Lq, dims, out.data_ptr(),
+                                         s.cuda_stream)
     if status != 0:
         raise MsdaError(status, status_string(status))
     return out

@@ -1,6 +1,8 @@
-// C ABI of the query-order builder (declared in include/msda.h): a Z-order
-// (Morton) visit order for queries that are the pyramid's pixel centres.
+// C ABI of the query-order builders (declared in include/msda.h): a Z-order
+// (Morton) visit order for queries that are the pyramid's pixel centres, and
+// one for queries given by a point each (data-dependent reference points).
 //
+// Pixel centres:
 // Every pixel gets the cell of a 2^kCellBits-per-axis grid over the unit
 // square (cube) that holds its normalized centre, and the pixels are ranked by
 // (Morton key of the cell, level, index in the level), or by (level, key,
@@ -136,6 +138,76 @@ __global__ __launch_bounds__(kThreads) void query_order_kernel(OrderParams op, i
     if (rank < op.S) order[rank] = static_cast<int32_t>(q);
 }
 
+// ---- Queries given by one point each.  The cell of a coordinate x on a grid
+// of 2^B cells over [0, 1] is floor(x * 2^B) (an exact product in fp32),
+// clamped to [0, 2^B - 1], NaN taken as 0; B = 16 in 2D, 10 in 3D.
+template <int DIM>
+__device__ __forceinline__ uint32_t point_cell(float x) {
+    constexpr int kBits = DIM == 2 ? 16 : 10;
+    const float scaled = x * static_cast<float>(1u << kBits);
+    float f = scaled == scaled ? floorf(scaled) : 0.0f;
+    f = fminf(fmaxf(f, 0.0f), static_cast<float>((1u << kBits) - 1u));
+    return static_cast<uint32_t>(f);
+}
+
+// Bit interleaving by successive shifts and masks (each step moves the upper
+// half of every bit group up by half the group's new spacing): bit b of a
+// 16-bit value to bit 2b, of a 10-bit value to bit 3b.
+__device__ __forceinline__ uint32_t spread_by_2(uint32_t v) {
+    v &= 0xffffu;
+    v = (v | (v << 8)) & 0x00ff00ffu;
+    v = (v | (v << 4)) & 0x0f0f0f0fu;
+    v = (v | (v << 2)) & 0x33333333u;
+    v = (v | (v << 1)) & 0x55555555u;
+    return v;
+}
+__device__ __forceinline__ uint32_t spread_by_3(uint32_t v) {
+    v &= 0x3ffu;
+    v = (v | (v << 16)) & 0x030000ffu;
+    v = (v | (v << 8)) & 0x0300f00fu;
+    v = (v | (v << 4)) & 0x030c30c3u;
+    v = (v | (v << 2)) & 0x09249249u;
+    return v;
+}
+
+// Morton key of point j: cell bit b of axis d at key bit DIM*b + d.
+template <int DIM>
+__device__ __forceinline__ uint32_t point_key(const float* pts, uint32_t j) {
+    const float* pj = pts + static_cast<size_t>(j) * DIM;
+    if constexpr (DIM == 2)
+        return spread_by_2(point_cell<2>(pj[0])) | (spread_by_2(point_cell<2>(pj[1])) << 1);
+    else
+        return spread_by_3(point_cell<3>(pj[0])) | (spread_by_3(point_cell<3>(pj[1])) << 1) |
+               (spread_by_3(point_cell<3>(pj[2])) << 2);
+}
+
+// One thread per query counts the queries that rank before it by (key,
+// index): the block loads the keys a tile at a time into LDS and every thread
+// compares its own against the tile (broadcast reads).  O(n^2) comparisons,
+// no sort and no scratch memory; it writes its index at its rank.
+template <int DIM>
+__global__ __launch_bounds__(kThreads) void points_order_kernel(const float* pts, uint32_t n,
+                                                                int32_t* order) {
+    __shared__ uint32_t tile[kThreads];
+    const uint32_t q = blockIdx.x * kThreads + threadIdx.x;
+    const bool live = q < n;
+    const uint32_t mine = live ? point_key<DIM>(pts, q) : 0u;
+    uint32_t rank = 0;
+    for (uint32_t t0 = 0; t0 < n; t0 += kThreads) {
+        __syncthreads();   // the previous tile is consumed
+        const uint32_t j = t0 + threadIdx.x;
+        tile[threadIdx.x] = j < n ? point_key<DIM>(pts, j) : 0u;
+        __syncthreads();
+        const uint32_t m = min(static_cast<uint32_t>(kThreads), n - t0);
+#pragma unroll 8
+        for (uint32_t i = 0; i < m; ++i) {
+            const uint32_t k = tile[i];
+            rank += (k < mine || (k == mine && t0 + i < q)) ? 1u : 0u;
+        }
+    }
+    if (live) order[rank] = static_cast<int32_t>(q);
+}
+
 }  // namespace
 
 extern "C" {
@@ -179,6 +251,28 @@ int msda_query_order(const int64_t* spatial_shapes, int64_t L, int64_t dims, int
                            query_order);
     else
         hipLaunchKernelGGL(query_order_kernel<3>, dim3(blocks), dim3(kThreads), 0, hs, op,
+                           query_order);
+    if (hipGetLastError() != hipSuccess) return MSDA_ERR_LAUNCH;
+    return MSDA_OK;
+}
+
+int msda_query_order_points(const float* points, int64_t Lq, int64_t dims,
+                            int32_t* query_order, void* stream) {
+    if ((dims != 2 && dims != 3) || Lq < 0) return MSDA_ERR_DIM;
+    if (Lq == 0) return MSDA_OK;
+    if (!points || !query_order) return MSDA_ERR_NULL;
+    if (!msda_host::aligned(points, 4) || !msda_host::aligned(query_order, 4)) return MSDA_ERR_ALIGN;
+    // 32-bit query indices and point offsets
+    if (Lq >= (int64_t{1} << 30)) return MSDA_ERR_OVERFLOW;
+
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    const uint32_t n = static_cast<uint32_t>(Lq);
+    const uint32_t blocks = (n + kThreads - 1) / kThreads;
+    if (dims == 2)
+        hipLaunchKernelGGL(points_order_kernel<2>, dim3(blocks), dim3(kThreads), 0, hs, points, n,
+                           query_order);
+    else
+        hipLaunchKernelGGL(points_order_kernel<3>, dim3(blocks), dim3(kThreads), 0, hs, points, n,
                            query_order);
     if (hipGetLastError() != hipSuccess) return MSDA_ERR_LAUNCH;
     return MSDA_OK;

@@ -285,3 +285,23 @@ def test_query_order_builder_checks(lib):
     assert call_order(wptr, 1, 2, 1, A, 1 << 20) == UNSUP   # extent >= 2^20
     huge, hptr = _shapes_array([[1 << 19, 1 << 19]])
     assert call_order(hptr, 1, 2, 0, A, 1 << 38) == OVERFLOW
+
+
+def test_points_order_builder_checks(lib):
+    call_pts = binding.raw_query_order_points_call
+    assert call_pts(A, 10, 4, A) == DIM                 # dims not 2 or 3
+    assert call_pts(A, -1, 2, A) == DIM
+    assert call_pts(0, 0, 2, 0) == OK                    # empty: a no-op, pointers unused
+    assert call_pts(0, 10, 2, A) == NULL
+    assert call_pts(A, 10, 3, 0) == NULL
+    assert call_pts(A + 2, 10, 2, A) == ALIGN
+    assert call_pts(A, 10, 2, A + 2) == ALIGN
+    assert call_pts(A, 1 << 30, 2, A) == OVERFLOW
+
+
+def test_points_order_binding_rejects_bad_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        binding.msda_query_order_points(torch.zeros(10, 2))          # not on a GPU
+    with pytest.raises(ValueError):
+        binding.msda_query_order_points(torch.zeros(10, 4))

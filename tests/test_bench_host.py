@@ -25,3 +25,8 @@ def test_explicit_orders():
     assert bench.resolve_query_order("none", dec, "forward") == "none"
     assert bench.resolve_query_order("levels", enc, "forward_pruned") == "levels"
     assert bench.resolve_query_order("interleaved", dec, "forward") is None
+
+
+def test_points_order_is_allowed_for_any_queries():
+    for name in ("detr_decoder", "tiny", "detr_encoder", "volume3d"):
+        assert bench.resolve_query_order("points", CONFIGS[name], "forward") == "points"

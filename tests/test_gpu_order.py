@@ -6,7 +6,8 @@ call without one.  The order changes only which wave visits a query, never the
 arithmetic of a query, so every forward output and the location and weight
 gradients must be bit-identical; grad_value (fp32 atomics) is checked against
 the oracle with the backward's own bounds.  Orders come from the builder for
-pixel-centre queries and are random permutations otherwise; the cases cover
+pixel-centre queries, and from the points builder (on the first image's first
+sampling locations) or a random permutation otherwise; the cases cover
 the direct and the LDS-staged forward kernels, the de-duplicating backward,
 2D and 3D, fp32 and bf16.
 """
@@ -14,11 +15,12 @@ import numpy as np
 import pytest
 import torch
 
-from oracle.order import query_order_oracle
+from oracle.order import points_order_oracle, query_order_oracle
 from scale_deformable_attention_02_amd import (msda3d_backward, msda3d_forward,
                                                msda3d_forward_fused, msda3d_forward_pruned,
                                                msda_backward, msda_forward, msda_forward_fused,
-                                               msda_forward_pruned, msda_query_order)
+                                               msda_forward_pruned, msda_query_order,
+                                               msda_query_order_points)
 from scale_deformable_attention_02_amd.workloads import (CONFIGS, Workload, make_fused_inputs,
                                                          make_grad_out, make_inputs)
 from test_gpu_backward import check_backward
@@ -66,8 +68,46 @@ def test_order_builder_reuses_out_and_runs_on_a_side_stream():
     assert np.array_equal(out.cpu().numpy(), query_order_oracle(shapes, False))
 
 
+def _points(n, dims, seed):
+    """Points of every kind the builder must rank like the oracle: uniform,
+    clustered (equal cells), exact duplicates, values on cell edges, outside
+    [0, 1], infinite and NaN."""
+    g = np.random.default_rng(seed)
+    pts = g.random((n, dims)).astype(np.float32)
+    if n >= 64:
+        pts[: n // 4] = (0.5 + 1e-4 * g.standard_normal((n // 4, dims))).astype(np.float32)
+        pts[n // 4: n // 4 + 8] = pts[0]
+        pts[40] = 0.25
+        pts[41] = (-0.5, 1.5, 0.75)[:dims]
+        pts[42] = (np.inf, -np.inf, np.nan)[:dims]
+        pts[43] = (np.nan, 0.1, 2.0)[:dims]
+        pts[44] = 1.0
+    return pts
+
+
+@pytest.mark.parametrize("dims", [2, 3])
+@pytest.mark.parametrize("n", [1, 2, 255, 256, 257, 3001, 22223])
+def test_points_order_builder_matches_oracle(dims, n):
+    _log(f"[order] points builder dims={dims} n={n}")
+    pts = _points(n, dims, 100 + n + dims)
+    got = msda_query_order_points(torch.from_numpy(pts).to(DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy().astype(np.int64), points_order_oracle(pts))
+
+
+def test_points_order_builder_reuses_out_on_a_side_stream():
+    pts = torch.from_numpy(_points(1000, 2, 5)).to(DEV)
+    out = torch.full((1000,), -1, dtype=torch.int32, device=DEV)
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        got = msda_query_order_points(pts, out=out, stream=side)
+    side.synchronize()
+    assert got.data_ptr() == out.data_ptr()
+    assert np.array_equal(out.cpu().numpy(), points_order_oracle(pts.cpu().numpy()))
+
+
 # Cases: (label, workload).  Pixel-centre workloads take the builder's orders,
-# the others a random permutation.
+# the others the points builder's order and a random permutation.
 CASES = [
     ("2d-direct-pixel", Workload("o1", 2, 2, ((20, 33), (10, 17), (5, 9), (3, 5)), None, 8, 32,
                                  4, "f32", "pixel_centres", 0.03, (0, 1), 31)),
@@ -90,7 +130,10 @@ def _orders(w):
                 ("morton-interleaved", msda_query_order(w.shapes, False, device=DEV))]
     g = torch.Generator().manual_seed(w.seed)
     perm = torch.randperm(w.queries_per_image, generator=g).to(torch.int32)
-    return [("random", perm.to(DEV))]
+    # the first image's first sampling location of every query (head 0,
+    # level 0, point 0) as its point
+    loc = make_inputs(w)["sampling_locations"][0, :, 0, 0, 0, :].contiguous()
+    return [("points", msda_query_order_points(loc.to(DEV))), ("random", perm.to(DEV))]
 
 
 def _to_dev(inp):
