@@ -582,16 +582,30 @@ __device__ __forceinline__ Slot<NC> dead_slot(uint32_t invalid) {
 template <int DIM, int CPL>
 constexpr int direct_waves_per_eu() { return DIM == 3 && CPL >= 8 && CPL <= 32 ? 8 : 1; }
 
+// Waves per workgroup.  A workgroup's waves visit consecutive queries, so at
+// 8 waves per SIMD two 16-wave workgroups per CU keep fewer, larger
+// neighbourhoods of a volume in the CU's L1 than eight 4-wave ones: 1436
+// against 1504 us on the 64^3..8^3 volume.  The fused and pruned variants,
+// whose waves reach phase B at more uneven times, do best with 8 (1486
+// against 1530 us and 1049 against 1072 us; 16 gives 1530 and 1132 us).
+// Kernels below 8 waves per SIMD keep 4-wave workgroups, which fill the
+// SIMDs in finer steps.
+__host__ __device__ constexpr int direct_waves_per_block(int dim, int cpl, bool fused,
+                                                         bool prune) {
+    return dim == 3 && cpl >= 8 && cpl <= 32 ? (fused || prune ? 8 : 16) : kWavesPerBlock;
+}
+
 template <typename TV, typename TO, int DIM, int CPL, bool FUSED = false, bool PRUNE = false>
-__global__ __launch_bounds__(kBlockThreads)
+__global__ __launch_bounds__(kWave * direct_waves_per_block(DIM, CPL, FUSED, PRUNE))
 __attribute__((amdgpu_waves_per_eu(direct_waves_per_eu<DIM, CPL>())))
 void msda_forward_kernel(Params p) {
     constexpr int NC = DIM == 2 ? 4 : 8;     // corners per sample
     constexpr int NG = kWave / CPL;          // point groups per wave
     constexpr int VEC = ValueTraits<TV>::kVec;
+    constexpr int WPB = direct_waves_per_block(DIM, CPL, FUSED, PRUNE);
 
     __shared__ LevelGeom smeta[kMaxSamplesPerTile];   // level of sample s
-    __shared__ Slot<NC> slots[kWavesPerBlock][kWave];
+    __shared__ Slot<NC> slots[WPB][kWave];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -605,7 +619,7 @@ void msda_forward_kernel(Params p) {
     // wave -> slice (n, m) and first query q0, all wave-uniform
     const uint32_t blk = xcd_contiguous_block(blockIdx.x, p.num_blocks);
     const uint32_t wave_id =
-        __builtin_amdgcn_readfirstlane(blk * kWavesPerBlock + static_cast<uint32_t>(wave));
+        __builtin_amdgcn_readfirstlane(blk * WPB + static_cast<uint32_t>(wave));
     const bool wave_live = wave_id < p.waves;
     const uint32_t slice = fast_div(wave_id, p.div_wps);
     const uint32_t q0 = (wave_id - slice * p.wps) * static_cast<uint32_t>(p.T);

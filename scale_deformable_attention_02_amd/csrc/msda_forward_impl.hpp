@@ -48,8 +48,9 @@ using msda_host::make_fast_div;
 // Variants: plain forward, fused front end, pruned forward (never both).
 template <typename TV, typename TO, int DIM, int CPL, bool FUSED, bool PRUNE>
 void launch_one(const Params& p, hipStream_t stream) {
+    constexpr int wpb = msda::direct_waves_per_block(DIM, CPL, FUSED, PRUNE);
     hipLaunchKernelGGL((msda::msda_forward_kernel<TV, TO, DIM, CPL, FUSED, PRUNE>),
-                       dim3(p.num_blocks), dim3(msda::kBlockThreads), 0, stream, p);
+                       dim3(p.num_blocks), dim3(msda::kWave * wpb), 0, stream, p);
 }
 
 template <typename TV, typename TO, int DIM, int CPL, bool FUSED, bool PRUNE>
@@ -208,8 +209,8 @@ int forward(const void* value, int value_dtype, const int64_t* spatial_shapes,
             p.head_bytes = static_cast<uint32_t>(head_bytes);
             p.out_head_bytes = static_cast<uint32_t>(out_head_bytes);
             p.image_bytes = static_cast<uint32_t>(image_bytes);
-            p.num_blocks = static_cast<uint32_t>((waves + msda::kWavesPerBlock - 1) /
-                                                 msda::kWavesPerBlock);
+            const int wpb = msda::direct_waves_per_block(DIM, cpl, FUSED, PRUNE);
+            p.num_blocks = static_cast<uint32_t>((waves + wpb - 1) / wpb);
             p.waves = static_cast<uint32_t>(waves);
             p.M = static_cast<int32_t>(M);
             p.Lq = static_cast<int32_t>(Lq);
