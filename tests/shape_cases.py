@@ -2,7 +2,8 @@
 
 SMALL: multi-tile problems with ragged tails over the launch-shape space
 (chunks per head row 1..64 incl. non powers of two, L*P from 1 to 64, fp32 and
-bf16 value, 2D and 3D, batch > 1, Lq a multiple of no tile count).
+bf16 value, 2D and 3D with rows of up to 64 chunks, batch > 1, Lq a multiple
+of no tile count).
 
 STAGED: launches of >= 65536 (query, head) tiles: levels that fit the LDS
 budget of the staged forward kernel or not, fp32/bf16, D from 4 to 64
@@ -26,6 +27,12 @@ SMALL = [
     (3, "f32", 2, ((8, 8, 8), (4, 4, 4), (2, 2, 2)), 219, 4, 32, 4),
     (3, "bf16", 1, ((6, 7, 9), (3, 4, 5)), 111, 8, 32, 3),
     (3, "f32", 1, ((3, 5, 7),), 37, 3, 8, 7),
+    # 3D head rows of 32 and 64 chunks (fp32 D = 128 and 256, bf16 D = 256):
+    # the widest rows of the 16-wave (8-wave fused/pruned) direct blocks, and
+    # the 4-wave blocks beyond them
+    (3, "f32", 1, ((5, 6, 7), (3, 3, 4)), 77, 2, 128, 3),
+    (3, "bf16", 2, ((4, 5, 6),), 45, 3, 256, 2),
+    (3, "f32", 1, ((3, 4, 5), (2, 2, 2)), 29, 2, 256, 2),
 ]
 
 STAGED = [
