@@ -315,7 +315,8 @@ int msda_query_order(const int64_t* spatial_shapes, int64_t L, int64_t dims,
  * so nothing is sorted and nothing is allocated.  Asynchronous on `stream`.
  * Lq == 0 is a successful no-op.
  * Errors: MSDA_ERR_DIM (dims not 2 or 3, Lq < 0); MSDA_ERR_NULL;
- * MSDA_ERR_ALIGN; MSDA_ERR_OVERFLOW (Lq >= 2^30); MSDA_ERR_LAUNCH.
+ * MSDA_ERR_ALIGN; MSDA_ERR_UNSUPPORTED (Lq > 2^21, where the quadratic
+ * count would take about half a second or more); MSDA_ERR_LAUNCH.
  */
 int msda_query_order_points(const float* points, int64_t Lq, int64_t dims,
                             int32_t* query_order, void* stream);

@@ -481,8 +481,9 @@ def msda_query_order_points(points, out=None, stream=None) -> torch.Tensor:
     reference points): int32 [Lq], the queries ranked by (Z-order key of the
     point's cell on a 2^16 (2D) or 2^10 (3D) grid per axis, query index).
     ``points`` is a float32 GPU tensor [Lq, 2] = (x, y) or [Lq, 3] =
-    (x, y, z) in normalized coordinates.  The order is one permutation for all
-    images of a call, so pass the points of the image it should follow."""
+    (x, y, z) in normalized coordinates, at most 2^21 of them (the rank
+    count is quadratic).  The order is one permutation for all images of a
+    call, so pass the points of the image it should follow."""
     if (not isinstance(points, torch.Tensor) or not points.is_cuda or points.dim() != 2
             or points.shape[1] not in (2, 3) or points.dtype != torch.float32):
         raise ValueError("points must be a float32 GPU tensor [Lq, 2] or [Lq, 3]")

@@ -31,6 +31,8 @@ constexpr int kCellBits = 10;
 constexpr int kMaxLevels = 16;
 constexpr int kMaxExtent = 1 << 20;
 constexpr int kThreads = 256;
+// Most queries msda_query_order_points ranks (its work grows as Lq^2).
+constexpr int64_t kMaxPointsOrderQueries = int64_t{1} << 21;
 
 struct OrderParams {
     uint32_t ext[kMaxLevels][3];      // per level: extent along x, y, z (1 in 2D)
@@ -262,8 +264,8 @@ int msda_query_order_points(const float* points, int64_t Lq, int64_t dims,
     if (Lq == 0) return MSDA_OK;
     if (!points || !query_order) return MSDA_ERR_NULL;
     if (!msda_host::aligned(points, 4) || !msda_host::aligned(query_order, 4)) return MSDA_ERR_ALIGN;
-    // 32-bit query indices and point offsets
-    if (Lq >= (int64_t{1} << 30)) return MSDA_ERR_OVERFLOW;
+    // the rank count is quadratic: 2^21 queries take about half a second
+    if (Lq > kMaxPointsOrderQueries) return MSDA_ERR_UNSUPPORTED;
 
     const hipStream_t hs = static_cast<hipStream_t>(stream);
     const uint32_t n = static_cast<uint32_t>(Lq);

@@ -296,7 +296,8 @@ def test_points_order_builder_checks(lib):
     assert call_pts(A, 10, 3, 0) == NULL
     assert call_pts(A + 2, 10, 2, A) == ALIGN
     assert call_pts(A, 10, 2, A + 2) == ALIGN
-    assert call_pts(A, 1 << 30, 2, A) == OVERFLOW
+    assert call_pts(A, (1 << 21) + 1, 2, A) == UNSUP     # quadratic cost past 2^21 queries
+    assert call_pts(A, 1 << 30, 3, A) == UNSUP
 
 
 def test_points_order_binding_rejects_bad_tensors():
