@@ -1,4 +1,5 @@
-"""Host logic of the benchmark (CPU): the visit order each run uses."""
+"""Host logic of the benchmark (CPU): the visit order each run uses, and the
+committed counters it reads."""
 import pytest
 
 import bench
@@ -30,3 +31,13 @@ def test_explicit_orders():
 def test_points_order_is_allowed_for_any_queries():
     for name in ("detr_decoder", "tiny", "detr_encoder", "volume3d"):
         assert bench.resolve_query_order("points", CONFIGS[name], "forward") == "points"
+
+
+def test_committed_counters_match_the_kernel_sources():
+    # roofline.traffic of the headline line comes from profiles/*_counters.json,
+    # taken on the kernel sources as they are; a kernel change needs new
+    # counters (the bench line reports traffic as null until then)
+    interleaved = "z-order, levels interleaved"
+    assert bench.counters_for("detr_encoder", "forward", interleaved) is not None
+    assert bench.counters_for("volume3d", "forward", interleaved) is not None
+    assert bench.counters_for("detr_encoder", "backward", interleaved) is not None
