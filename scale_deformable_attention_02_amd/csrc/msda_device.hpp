@@ -857,7 +857,12 @@ void msda_forward_staged_kernel(StagedParams sp) {
         const uint32_t out_row =
             (image_q0 + query_at(p, q0 + static_cast<uint32_t>(tb))) * static_cast<uint32_t>(p.M) + m;
 
-        // ---- Phase A
+        // ---- Phase A, at a raised wave priority: the arbiter then issues the
+        // slot writes and the next chunk's location loads ahead of the other
+        // waves' gathers (encoder 111.3 against 113.3 us, fused 116.2 against
+        // 118.8 us, pruned 105.6 against 106.6 us; the same in the direct 3D
+        // kernel was slower)
+        __builtin_amdgcn_s_setprio(1);
         if constexpr (FUSED) finish_sample_fused<DIM, ilog2<NG>()>(live, p.log2G, xyz, a, ref);
         const Slot<NC> sl = make_slot<DIM>(xyz, a, live, lga, slot_base, slot_stride, slot_invalid);
         const int hbm_end = ni_hbm, lds_end = NI;
@@ -880,6 +885,7 @@ void msda_forward_staged_kernel(StagedParams sp) {
             q_next = query_at(p, q0 + stride + static_cast<uint32_t>(ta));
         }
         wave_lds_sync();
+        __builtin_amdgcn_s_setprio(0);
 
         // ---- Phase B
         float acc[VEC];
