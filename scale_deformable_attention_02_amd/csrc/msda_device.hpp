@@ -773,8 +773,11 @@ void msda_forward_staged_kernel(StagedParams sp) {
     }
     __syncthreads();
     if (tid == 0) {
+        // HBM levels coarse to fine (measured 0.5-1.5% faster than fine to
+        // coarse on the encoder, fused and bf16 N=8 workloads), then the
+        // staged ones
         int k = 0;
-        for (int l = 0; l < p.L; ++l)
+        for (int l = p.L - 1; l >= 0; --l)
             if (level_lds[l] < 0)
                 for (int it = 0; it < sp.ipl; ++it) iter_of[k++] = l * sp.ipl + it;
         n_hbm_iters = k;
