@@ -235,6 +235,7 @@ def gather_ceilings(dev, windows=CALIB_WINDOWS, lds_modes=CALIB_LDS_MODES, strea
     import torch
 
     from scale_deformable_attention_02_amd.binding import (calib_gather_global,
+                                                           calib_gather_global_lds,
                                                            calib_gather_lds, calib_stream)
 
     blocks = NUM_CUS * 8
@@ -265,6 +266,9 @@ def gather_ceilings(dev, windows=CALIB_WINDOWS, lds_modes=CALIB_LDS_MODES, strea
         if name in ("l1", "l2"):   # the same rows read half a row per 4 lanes
             out[name + "_half_rows"] = timed(
                 lambda: calib_gather_global(buf, wb, blocks, iters, sink, lanes_per_row=4))
+            # the same rows into LDS by the loads' LDS mode, then read back
+            out[name + "_via_lds_dma"] = timed(
+                lambda: calib_gather_global_lds(buf, wb, blocks, iters, sink))
     for name, mode in lds_modes.items():
         out[name] = timed(lambda: calib_gather_lds(buf, mode, blocks, 4096, sink))
     out["hbm_stream"] = timed(lambda: calib_stream(buf, stream_bytes, blocks, sink))

@@ -38,6 +38,13 @@ extern "C" {
 int msda_calib_gather_global(const void* buf, uint64_t window_bytes, int lanes_per_row,
                              int blocks, int iters, void* sink, void* stream);
 
+/* The rows of msda_calib_gather_global with 8 lanes per row, delivered into
+ * LDS by the buffer load's LDS mode instead of into registers (window_bytes a
+ * power of two, 128 .. 2^30), then read back from LDS, 16 bytes per lane:
+ * the rate of the other path from the L1 to a kernel's lanes. */
+int msda_calib_gather_global_lds(const void* buf, uint64_t window_bytes, int blocks, int iters,
+                                 void* sink, void* stream);
+
 /* 16-byte reads from a 64 KB LDS array (512 rows of 128 bytes plus one spare
  * row) filled from `fill` (at least 65664 bytes), each group of 8 lanes:
  * mode 0 one random row; mode 1 rows in x-adjacent pairs (the groups 2h and

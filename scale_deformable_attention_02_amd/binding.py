@@ -39,7 +39,8 @@ STATUS = {
 EXPORTED = ("msda_forward", "msda3d_forward", "msda_forward_pruned", "msda3d_forward_pruned",
             "msda_forward_fused", "msda3d_forward_fused", "msda_backward", "msda3d_backward",
             "msda_linear", "msda_query_order", "msda_query_order_points", "msda_status_string",
-            "msda_calib_gather_global", "msda_calib_gather_lds", "msda_calib_stream")
+            "msda_calib_gather_global", "msda_calib_gather_global_lds", "msda_calib_gather_lds",
+            "msda_calib_stream")
 
 _lib = None
 
@@ -100,6 +101,8 @@ def load_library() -> ctypes.CDLL:
     ci = ctypes.c_int
     lib.msda_calib_gather_global.restype = ci
     lib.msda_calib_gather_global.argtypes = [vp, u64, ci, ci, ci, vp, vp]
+    lib.msda_calib_gather_global_lds.restype = ci
+    lib.msda_calib_gather_global_lds.argtypes = [vp, u64, ci, ci, vp, vp]
     lib.msda_calib_gather_lds.restype = ci
     lib.msda_calib_gather_lds.argtypes = [vp, ci, ci, ci, vp, vp]
     lib.msda_calib_stream.restype = ci
@@ -525,6 +528,19 @@ def calib_gather_global(buf: torch.Tensor, window_bytes: int, blocks: int, iters
     st = lib.msda_calib_gather_global(buf.data_ptr(), window_bytes, lanes_per_row, blocks, iters,
                                       sink.data_ptr(), torch.cuda.current_stream().cuda_stream)
     _calib_check(st, "msda_calib_gather_global")
+    return blocks * CALIB_THREADS * iters * 16
+
+
+def calib_gather_global_lds(buf: torch.Tensor, window_bytes: int, blocks: int, iters: int,
+                            sink: torch.Tensor) -> int:
+    """The rows of ``calib_gather_global`` (8 lanes per row) delivered into
+    LDS by the loads' LDS mode, then read back from LDS."""
+    lib = load_library()
+    assert buf.is_cuda and sink.is_cuda and buf.numel() * buf.element_size() >= window_bytes
+    assert sink.numel() * sink.element_size() >= blocks * CALIB_THREADS * 16
+    st = lib.msda_calib_gather_global_lds(buf.data_ptr(), window_bytes, blocks, iters,
+                                          sink.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    _calib_check(st, "msda_calib_gather_global_lds")
     return blocks * CALIB_THREADS * iters * 16
 
 

@@ -6,6 +6,8 @@
 //     Infinity Cache (32 MB) or spans HBM (1 GB and more);
 //   - LDS: random rows, rows read in x-adjacent pairs by 16 lanes, and a
 //     16-byte broadcast to every 8 lanes (the pattern of a shared slot);
+//   - the same global rows delivered into LDS by the buffer load's LDS mode
+//     (no VGPR on the way) and read back with ds_read_b128;
 //   - a coalesced HBM read stream, as the reference for HBM bandwidth.
 // These are measurement kernels, not part of the operator.  Every load is in
 // bounds: row indices are masked to the (power-of-two) window.
@@ -51,6 +53,41 @@ __global__ __launch_bounds__(kThreads) void gather_global_kernel(const uint4* bu
         for (int u = 0; u < kUnroll; ++u) acc += v[u];
     }
     if (acc == 0x12345678u) sink[tid] = make_uint4(acc, 0, 0, 0);   // keeps the loads
+}
+
+// Random 128-byte rows as in gather_global_kernel<false>, delivered into LDS
+// by buffer_load_dwordx4 ... lds: lane l of a wave writes its 16 bytes at
+// byte 16 l of that load's 1 KB slice of the wave's LDS area, kUnroll slices
+// per wave.  After the loads complete, each lane reads its 16 bytes of every
+// slice back with ds_read_b128 (the path a kernel would take to use them).
+__global__ __launch_bounds__(kThreads) void gather_global_lds_kernel(const uint4* buf,
+                                                                    uint32_t row_mask, int iters,
+                                                                    uint4* sink) {
+    __shared__ __align__(16) uint4 area[kThreads / 64][kUnroll][64];   // 32 KB
+    const uint32_t tid = blockIdx.x * kThreads + threadIdx.x;
+    const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t c = threadIdx.x & 7;
+    uint32_t r = lcg(tid >> 3) ^ 0x9e3779b9u;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint4*>(buf), 0, static_cast<int>((row_mask + 1u) * 128u), 0x00020000);
+    uint32_t acc = 0;
+    for (int i = 0; i < iters; i += kUnroll) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            r = lcg(r);
+            const uint32_t off = ((r >> 7) & row_mask) * 128u + c * 16u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, &area[wave][u][0], 16, off, 0, 0, 0);
+        }
+        __builtin_amdgcn_s_waitcnt(0);   // the LDS writes of this wave's loads are done
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const uint4 x = area[wave][u][lane];
+            acc += x.x ^ x.y ^ x.z ^ x.w;
+        }
+        __builtin_amdgcn_s_waitcnt(0);   // reads done before the next loads overwrite
+        __builtin_amdgcn_wave_barrier();
+    }
+    if (acc == 0x12345678u) sink[tid] = make_uint4(acc, 0, 0, 0);
 }
 
 // LDS patterns over a 64 KB array (512 rows of 128 bytes, plus one spare
@@ -156,6 +193,19 @@ int msda_calib_gather_global(const void* buf, uint64_t window_bytes, int lanes_p
     else
         hipLaunchKernelGGL(gather_global_kernel<true>, dim3(blocks), dim3(kThreads), 0, s,
                            static_cast<const uint4*>(buf), mask, iters, static_cast<uint4*>(sink));
+    return hipGetLastError() == hipSuccess ? MSDA_OK : MSDA_ERR_LAUNCH;
+}
+
+int msda_calib_gather_global_lds(const void* buf, uint64_t window_bytes, int blocks, int iters,
+                                 void* sink, void* stream) {
+    if (!buf || !sink) return MSDA_ERR_NULL;
+    if (!pow2(window_bytes) || window_bytes < 128 || window_bytes > (uint64_t{1} << 30) ||
+        blocks < 1 || iters < kUnroll || iters % kUnroll != 0)
+        return MSDA_ERR_DIM;
+    hipLaunchKernelGGL(gather_global_lds_kernel, dim3(blocks), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const uint4*>(buf),
+                       static_cast<uint32_t>(window_bytes / 128 - 1), iters,
+                       static_cast<uint4*>(sink));
     return hipGetLastError() == hipSuccess ? MSDA_OK : MSDA_ERR_LAUNCH;
 }
 
