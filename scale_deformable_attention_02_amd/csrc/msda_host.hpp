@@ -36,4 +36,13 @@ inline bool aligned(const void* ptr, uintptr_t a) {
     return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) == 0;
 }
 
+// Compute units of the current device (0 if the query fails).
+inline int device_cus() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    return cus;
+}
+
 }  // namespace msda_host

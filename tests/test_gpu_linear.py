@@ -92,3 +92,27 @@ def test_empty_rows():
     x = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
     w = torch.zeros((32, 64), dtype=torch.bfloat16, device=DEV)
     assert msda_linear(x, w).shape == (0, 32)
+
+
+# Launches that take the W-stationary bf16 kernel (bf16 x, K in {64, 128,
+# 256}, N <= 256, at least 65536 rows): ragged last 32-row tile, N not a
+# multiple of 8 or 4 (narrower stores), output columns past N in the last
+# consumer wave, and both output types.
+@pytest.mark.parametrize("R,K,N", [(65537, 256, 256), (70000, 128, 100), (66000, 64, 99),
+                                   (65571, 256, 136)])
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+def test_weight_stationary_shapes(R, K, N, out):
+    run(R, K, N, "bf16", out, bias=(N % 2 == 0))
+
+
+def test_weight_stationary_writes_stay_inside_y():
+    R, K, N = 65539, 256, 136
+    inp = make_linear_inputs(R, K, N, "bf16", 7)
+    pad = 4096
+    buf = torch.full((pad + R * N + pad,), 7.0, device=DEV)
+    y = buf[pad:pad + R * N].view(R, N)
+    msda_linear(inp["x"].to(DEV), inp["weight"].to(DEV), inp["bias"].to(DEV), out=y)
+    torch.cuda.synchronize()
+    assert torch.all(buf[:pad] == 7.0) and torch.all(buf[-pad:] == 7.0)
+    ref = linear_oracle(inp["x"], inp["weight"], inp["bias"])
+    assert np.abs(y.cpu().double().numpy() - ref).max() < 1e-3
