@@ -2,11 +2,12 @@
 
 The library allocates, synchronises and memsets nothing (the backward clears
 grad_value with a fill kernel, not a memset node), so a sequence of calls can
-be captured once and replayed.  One graph holds the order builder, the plain,
-pruned and fused forwards, the backward and the value projection of an
-encoder-shaped pyramid large enough for the staged forward and the
-de-duplicating backward.  It is replayed several times, with new inputs
-copied into its tensors between the replays and the same calls made eagerly
+be captured once and replayed.  One graph holds the order builders, the plain,
+pruned and fused forwards and the backward of an encoder-shaped pyramid large
+enough for the staged forward and the de-duplicating backward, and two value
+projections (the tiled and the W-stationary kernel).  It is replayed several
+times, with new inputs copied into its tensors between the replays and the
+same calls made eagerly
 after each replay; every replay is checked against those eager results: bit
 for bit where the kernels are deterministic (forwards, order, location and
 weight gradients, projection), and grad_value, whose fp32 atomics add in any
@@ -41,7 +42,9 @@ def _draw(seed):
     inp = make_inputs(w)
     fin = make_fused_inputs(w)
     grad = make_grad_out(w)
-    lin = make_linear_inputs(64 * 37, 256, 256, "bf16", seed=seed)
+    # the tiled projection kernel, and (65,573 rows) the W-stationary one
+    lin = {"small": make_linear_inputs(64 * 37, 256, 256, "bf16", seed=seed),
+           "large": make_linear_inputs(65573, 256, 256, "bf16", seed=seed + 1)}
     return w, inp, fin, grad, lin
 
 
@@ -52,7 +55,7 @@ class Static:
         self.inp = {k: v.to(DEV) for k, v in inp.items()}
         self.fin = {k: v.to(DEV) for k, v in fin.items()}
         self.grad = grad.to(DEV)
-        self.lin = {k: v.to(DEV) for k, v in lin.items()}
+        self.lin = {n: {k: v.to(DEV) for k, v in d.items()} for n, d in lin.items()}
         # the points order follows each query's first sampling location
         self.points = inp["sampling_locations"][0, :, 0, 0, 0, :].contiguous().to(DEV)
         N, Lq, M, L, P, _ = inp["sampling_locations"].shape
@@ -67,8 +70,10 @@ class Static:
         self.gv = torch.empty(inp["value"].shape, **f32)
         self.gl = torch.empty(inp["sampling_locations"].shape, **f32)
         self.ga = torch.empty(inp["attention_weights"].shape, **f32)
-        self.y = torch.empty((lin["x"].shape[0], lin["weight"].shape[0]), dtype=torch.bfloat16,
-                             device=DEV)
+        self.y = torch.empty((lin["small"]["x"].shape[0], lin["small"]["weight"].shape[0]),
+                             dtype=torch.bfloat16, device=DEV)
+        self.y_large = torch.empty((lin["large"]["x"].shape[0], lin["large"]["weight"].shape[0]),
+                                   dtype=torch.bfloat16, device=DEV)
 
     def load(self, inp, fin, grad, lin):
         for k, v in inp.items():
@@ -76,8 +81,9 @@ class Static:
         for k, v in fin.items():
             self.fin[k].copy_(v)
         self.grad.copy_(grad)
-        for k, v in lin.items():
-            self.lin[k].copy_(v)
+        for n, d in lin.items():
+            for k, v in d.items():
+                self.lin[n][k].copy_(v)
         self.points.copy_(inp["sampling_locations"][0, :, 0, 0, 0, :])
 
     def run(self):
@@ -93,11 +99,13 @@ class Static:
                            out=self.out_fused, query_order=self.porder)
         msda_backward(*args, self.grad, grad_value=self.gv, grad_sampling_locations=self.gl,
                       grad_attention_weights=self.ga, query_order=self.order)
-        msda_linear(self.lin["x"], self.lin["weight"], self.lin["bias"], out=self.y)
+        for n, y in (("small", self.y), ("large", self.y_large)):
+            msda_linear(self.lin[n]["x"], self.lin[n]["weight"], self.lin[n]["bias"], out=y)
 
     def results(self):
         return {k: getattr(self, k).clone() for k in
-                ("order", "porder", "out", "out_pruned", "out_fused", "gv", "gl", "ga", "y")}
+                ("order", "porder", "out", "out_pruned", "out_fused", "gv", "gl", "ga", "y",
+                 "y_large")}
 
 
 def test_graph_replays_match_eager_calls():
@@ -131,7 +139,7 @@ def test_graph_replays_match_eager_calls():
         torch.cuda.synchronize()
         ref = eager_state.results()
 
-        for k in ("order", "porder", "out", "out_pruned", "out_fused", "gl", "ga", "y"):
+        for k in ("order", "porder", "out", "out_pruned", "out_fused", "gl", "ga", "y", "y_large"):
             assert torch.equal(got[k], ref[k]), f"replay {r}: {k} differs from the eager call"
 
         # grad_value: fp32 atomics add in any order; checked against the oracle
