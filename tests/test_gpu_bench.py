@@ -45,6 +45,10 @@ def test_bench_prints_one_json_line_with_the_contract_fields():
     assert cpu["single_core"]["cores"] == 1
     single = d["kernel_us_single"]
     assert 0 < single["min"] <= single["median"] <= single["p90"] <= single["max"]
+    # the encoder's visit order is built once, outside value, and said so
+    assert d["config"]["query_order"] != "none" and d["query_order_build_us"] > 0
+    assert d["value_includes_query_order_build"] is False
+    assert 0 < d["value_with_query_order_build_every_step"] < d["value"]
 
 
 def test_bench_refuses_more_than_one_gpu():
