@@ -20,12 +20,19 @@
 #include "msda_host.hpp"
 
 // Staged-kernel tuning (bytes of LDS for staged levels per workgroup,
-// workgroups sharing one (image, head) slice, smallest launch worth staging).
+// workgroups sharing one (image, head) slice for fp32 and for bf16 values,
+// smallest launch worth staging).  Same-process A/B timing: fp32 encoder
+// 105.1 us at 128 against 106.9 (96) and 107.6 (160, 192); bf16 N=8 302.1
+// us at 96 against 305.7 (64), 306.6 (80), 305.9 (112) and 307.6 (128), its
+// pruned forward 279.3 against 287.2 us (128).
 #ifndef MSDA_STAGE_BUDGET
 #define MSDA_STAGE_BUDGET (34 * 1024 + 512)
 #endif
 #ifndef MSDA_STAGED_WGS_PER_SLICE
 #define MSDA_STAGED_WGS_PER_SLICE 128
+#endif
+#ifndef MSDA_STAGED_WGS_PER_SLICE_BF16
+#define MSDA_STAGED_WGS_PER_SLICE_BF16 96
 #endif
 #ifndef MSDA_STAGED_MIN_TILES
 #define MSDA_STAGED_MIN_TILES 65536
@@ -243,7 +250,8 @@ int forward(const void* value, int value_dtype, const int64_t* spatial_shapes,
                 const int64_t pass = int64_t{msda::kStagedWaves} * T;
                 const int64_t slices = nbatch * M;
                 const int64_t chunks = (nquery + pass - 1) / pass;   // per slice
-                int64_t wgs_per_slice = MSDA_STAGED_WGS_PER_SLICE;
+                int64_t wgs_per_slice = value_dtype == MSDA_BF16 ? MSDA_STAGED_WGS_PER_SLICE_BF16
+                                                                 : MSDA_STAGED_WGS_PER_SLICE;
                 if (wgs_per_slice > chunks) wgs_per_slice = chunks;
                 int64_t stage = (S + 1) * head_bytes;
                 if (stage > MSDA_STAGE_BUDGET) stage = MSDA_STAGE_BUDGET;
